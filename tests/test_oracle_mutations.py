@@ -1,0 +1,143 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins fail.
+
+Each mutation swaps one oracle function for a subtly wrong version: a dropped
+term, a wrong sign or index, a transposed or swapped operand, a wrong tie rule.
+The pin helpers of test_oracle_pins must reject every one of them.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as mo
+from oracle import mx_oracle as mx
+
+import test_oracle_pins as pins
+
+
+def _fails(check, *args):
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        check(*args)
+
+
+def test_silu_replaced_by_sigmoid(monkeypatch):
+    monkeypatch.setattr(mo, "silu", lambda z: mo.sigmoid(z))
+    _fails(pins.check_forward, pins.oracle_out)
+
+
+def test_gate_and_up_swapped(monkeypatch):
+    orig = mo.expert_ffn_forward
+    monkeypatch.setattr(mo, "expert_ffn_forward",
+                        lambda x, o, wg, wu, wd: orig(x, o, wu, wg, wd))
+    _fails(pins.check_forward, pins.oracle_out)
+
+
+def test_combine_uses_wrong_slot_order(monkeypatch):
+    orig = mo.combine
+    monkeypatch.setattr(mo, "combine", lambda y, g, pd, k: orig(y, g[:, ::-1], pd, k))
+    _fails(pins.check_forward, pins.oracle_out)
+
+
+def test_dhg_missing_term(monkeypatch):
+    def bad(dy_perm, x_perm, offsets, wg, wu, wd):
+        X, dY = np.asarray(x_perm, float), np.asarray(dy_perm, float)
+        out = {"dx_perm": np.zeros_like(X), "dw_gate": np.zeros_like(wg), "dw_up": np.zeros_like(wu),
+               "dw_down": np.zeros_like(wd)}
+        for e in range(wg.shape[0]):
+            s = slice(int(offsets[e]), int(offsets[e + 1]))
+            hg, hu = X[s] @ wg[e], X[s] @ wu[e]
+            sg = mo.sigmoid(hg)
+            da = dY[s] @ wd[e].T
+            dhu = da * hg * sg
+            dhg = da * hu * sg  # the (1 + hg (1 - sg)) factor dropped
+            out["dx_perm"][s] = dhg @ wg[e].T + dhu @ wu[e].T
+            out["dw_down"][e] = (hg * sg * hu).T @ dY[s]
+            out["dw_gate"][e] = X[s].T @ dhg
+            out["dw_up"][e] = X[s].T @ dhu
+        return out
+    monkeypatch.setattr(mo, "expert_ffn_backward", bad)
+    _fails(pins.check_backward, pins.oracle_out)
+
+
+def test_wgrad_operands_swapped(monkeypatch):
+    orig = mo.expert_ffn_backward
+
+    def bad(*a):
+        r = orig(*a)
+        r["dw_gate"], r["dw_up"] = r["dw_up"], r["dw_gate"]
+        return r
+    monkeypatch.setattr(mo, "expert_ffn_backward", bad)
+    _fails(pins.check_backward, pins.oracle_out)
+
+
+def test_router_bwd_sign_flipped(monkeypatch):
+    orig = mo.topk_gates_backward
+    monkeypatch.setattr(mo, "topk_gates_backward", lambda g, dg, i, E: -orig(g, dg, i, E))
+    _fails(pins.check_backward, pins.oracle_out)
+
+
+def test_router_weight_grad_transposed_input(monkeypatch):
+    monkeypatch.setattr(mo, "router_logits_backward",
+                        lambda x, w, dl: (dl @ np.asarray(w).T, np.asarray(x).T @ dl[::-1]))
+    _fails(pins.check_backward, pins.oracle_out)
+
+
+def test_dispatch_bwd_uses_wrong_index(monkeypatch):
+    orig = mo.dispatch_backward
+    monkeypatch.setattr(mo, "dispatch_backward",
+                        lambda dX, pd, k: orig(dX, np.roll(pd, 1), k))
+    _fails(pins.check_backward, pins.oracle_out)
+
+
+def test_topk_tie_to_higher_index():
+    def bad(logits, k):
+        l32 = np.asarray(logits, np.float32)
+        E = l32.shape[1]
+        rev = np.argsort(-l32[:, ::-1], axis=1, kind="stable")
+        return (E - 1 - rev[:, :k]).astype(np.int32)
+    _fails(pins.check_topk, bad)
+
+
+def test_gates_not_renormalised():
+    def bad(logits, idx):
+        l64 = np.asarray(logits, np.float64)
+        full = np.exp(l64 - l64.max(axis=1, keepdims=True))
+        full /= full.sum(axis=1, keepdims=True)
+        return np.take_along_axis(full, np.asarray(idx, np.int64), axis=1)
+    _fails(pins.check_gates, bad)
+
+
+def test_metadata_token_major_order():
+    def bad(idx, E):
+        m = mo.routing_metadata(idx, E)
+        R = idx.size
+        m["perm_src"] = np.arange(R, dtype=np.int32)  # token-major instead of expert-major
+        m["perm_dst"] = np.arange(R, dtype=np.int32)
+        return m
+    _fails(pins.check_metadata, bad)
+
+
+def test_metadata_offsets_inclusive():
+    def bad(idx, E):
+        m = mo.routing_metadata(idx, E)
+        m["offsets"] = np.concatenate([np.cumsum(m["counts"]), [idx.size]]).astype(np.int32)
+        return m
+    _fails(pins.check_metadata, bad)
+
+
+def test_e4m3_round_half_up():
+    def bad(y):
+        y = np.asarray(y, np.float64)
+        a = np.abs(y)
+        _, ex = np.frexp(a)
+        p = np.maximum(ex - 1, -6)
+        q = np.ldexp(1.0, p - 3)
+        r = np.minimum(np.floor(a / q + 0.5) * q, 448.0)
+        return mx.e4m3_encode(np.where(np.signbit(y), -r, r))
+    _fails(pins.check_encode, bad)
+
+
+def test_e4m3_no_saturation():
+    def bad(y):
+        y = np.asarray(y, np.float64)
+        c = mx.e4m3_encode(y).astype(np.int64)
+        return np.where(np.abs(y) > 464, c | 0x7F, c).astype(np.uint8)  # NaN instead of 448
+    _fails(pins.check_encode, bad)
