@@ -173,10 +173,7 @@ def expert_ffn_forward(x_perm, offsets, w_gate, w_up, w_down):
     Returns dict h_gate, h_up, a_act [R, f] and y_perm [R, d] (fp64).
     """
     X = np.asarray(x_perm, np.float64)
-    Wg = np.asarray(w_gate, np.float64)
-    Wu = np.asarray(w_up, np.float64)
-    Wd = np.asarray(w_down, np.float64)
-    E, d, f = Wg.shape
+    E, d, f = np.shape(w_gate)
     R = X.shape[0]
     hg = np.zeros((R, f))
     hu = np.zeros((R, f))
@@ -186,10 +183,12 @@ def expert_ffn_forward(x_perm, offsets, w_gate, w_up, w_down):
         s = slice(int(offsets[e]), int(offsets[e + 1]))
         if s.start == s.stop:
             continue
-        hg[s] = X[s] @ Wg[e]
-        hu[s] = X[s] @ Wu[e]
+        # each expert's weights are converted to fp64 only when it has rows
+        Wg, Wu, Wd = (np.asarray(w[e], np.float64) for w in (w_gate, w_up, w_down))
+        hg[s] = X[s] @ Wg
+        hu[s] = X[s] @ Wu
         a[s] = silu(hg[s]) * hu[s]
-        y[s] = a[s] @ Wd[e]
+        y[s] = a[s] @ Wd
     return {"h_gate": hg, "h_up": hu, "a_act": a, "y_perm": y}
 
 
@@ -239,27 +238,25 @@ def expert_ffn_backward(dy_perm, x_perm, offsets, w_gate, w_up, w_down):
     """
     dY = np.asarray(dy_perm, np.float64)
     X = np.asarray(x_perm, np.float64)
-    Wg = np.asarray(w_gate, np.float64)
-    Wu = np.asarray(w_up, np.float64)
-    Wd = np.asarray(w_down, np.float64)
-    E, d, f = Wg.shape
+    E, d, f = np.shape(w_gate)
     R = X.shape[0]
     dx = np.zeros((R, d))
-    dwg = np.zeros_like(Wg)
-    dwu = np.zeros_like(Wu)
-    dwd = np.zeros_like(Wd)
+    dwg = np.zeros((E, d, f))
+    dwu = np.zeros((E, d, f))
+    dwd = np.zeros((E, f, d))
     for e in range(E):
         s = slice(int(offsets[e]), int(offsets[e + 1]))
         if s.start == s.stop:
             continue
-        hg = X[s] @ Wg[e]
-        hu = X[s] @ Wu[e]
+        Wg, Wu, Wd = (np.asarray(w[e], np.float64) for w in (w_gate, w_up, w_down))
+        hg = X[s] @ Wg
+        hu = X[s] @ Wu
         sg = sigmoid(hg)
         a = hg * sg * hu
-        da = dY[s] @ Wd[e].T
+        da = dY[s] @ Wd.T
         dhu = da * hg * sg
         dhg = da * hu * sg * (1.0 + hg * (1.0 - sg))
-        dx[s] = dhg @ Wg[e].T + dhu @ Wu[e].T
+        dx[s] = dhg @ Wg.T + dhu @ Wu.T
         dwd[e] = a.T @ dY[s]
         dwg[e] = X[s].T @ dhg
         dwu[e] = X[s].T @ dhu
