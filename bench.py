@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""MoE layer forward + backward throughput on one MI355X.
+
+One step is the whole hot path over one batch: router logits (linear-router
+workloads), top-k routing with device-built metadata, row-wise dispatch, the
+grouped SwiGLU expert FFN forward, the weighted combine, and all their
+backward passes.  Inputs are seeded synthetic tensors already resident in HBM
+when the timed region starts.  Default workload: bf16, T=8192 tokens, d=2048,
+E=8 experts, top-4, expert hidden 1024.
+
+Prints one JSON line.  The per-kernel times come from HIP events the library
+records around each of its launches during the timed steps; the CPU baseline
+is the fp64 oracle timed on a bounded token sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak), 1 GPU"
+PEAK = {"bf16": 2.5e15, "mxfp8": 5.0e15, "f32": 157.3e12}   # dense MFMA, FLOP/s
+HBM_PEAK = 8.0e12                                            # bytes/s
+
+
+def kernel_work(name: str, w, s: int) -> tuple[str, float]:
+    """Algorithmic work of one launch: ('mfma', flops) or ('hbm', bytes)."""
+    T, d, E, k, f, R = w.T, w.d, w.E, w.k, w.f, w.R
+    g = name.split("_")[0]
+    flops = {"G1": 4 * R * d * f, "G2": 2 * R * f * d, "G3": 2 * R * d * f, "G4": 2 * R * f * d,
+             "G5": 4 * R * f * d, "G6": 4 * R * d * f}
+    if g in flops:
+        return "mfma", float(flops[g])
+    hbm = {
+        "dispatch": T * d * s + R * d * s + 4 * R,
+        "combine": R * d * s + T * d * s + 8 * R,
+        "combine_bwd": T * d * s + 2 * R * d * s + 12 * R,
+        "dispatch_bwd": R * d * s + T * d * s + 4 * R,
+        "route_select": 4 * T * E + 12 * R,
+        "route_topk_bwd": 8 * R + 4 * T * E + 4 * R,
+    }
+    if name in hbm:
+        return "hbm", float(hbm[name])
+    return "other", 0.0
+
+
+def cpu_baseline(w, inp, target_s: float) -> dict:
+    """The oracle, untuned, on a bounded token sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as mo
+
+    def run(n):
+        t0 = time.perf_counter()
+        mo.layer_forward_backward(inp["x"][:n], inp["w_gate"], inp["w_up"], inp["w_down"], inp["dout"][:n], w.k,
+                                  logits=None if "w_router" in inp else inp["logits"][:n],
+                                  w_router=inp.get("w_router"))
+        return time.perf_counter() - t0
+
+    n0 = min(w.T, 256)
+    t0 = run(n0)
+    n = int(min(w.T, max(n0, (target_s / max(t0, 1e-3)) * n0)) // 64 * 64) or n0
+    t = run(n) if n != n0 else t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the same workload (all {w.E} experts, full d and f), "
+                      f"fp64 forward+backward, {t:.1f} s wall",
+            "numpy": np.__version__}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: bf16, E=8, top-4)")
+    ap.add_argument("--seed", type=int, default=17)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU are not "
+              "part of this build (no collectives, no sharding). Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from mixture_experts_layer_17_amd import binding as B
+    from mixture_experts_layer_17_amd import layer as L
+    from mixture_experts_layer_17_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    w = wl.WORKLOADS[args.workload]
+    print(f"# workload {w.name} {w.describe()}: generating inputs", file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w, seed=args.seed)
+    step = L.LayerStep(w, L.to_device(inp))
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    B.moe_timing_enable(True)
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+    B.moe_timing_report()  # discard warm-up records (the event pool is now warm)
+    print(f"# warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step.step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    kern = B.moe_timing_report()
+    B.moe_timing_enable(False)
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    s = 4 if w.storage == "f32" else 2
+    per_step_us = {name: 1e3 * ms / args.steps for name, (n, ms) in kern.items()}
+    per_launch_us = {name: 1e3 * ms / n for name, (n, ms) in kern.items()}
+    gemm_us = sum(v for kname, v in per_step_us.items() if kname[:2] in ("G1", "G2", "G3", "G4", "G5", "G6"))
+    gemm_flops = 18.0 * w.R * w.d * w.f
+    gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12 if gemm_us > 0 else None
+    dom = max(per_step_us, key=per_step_us.get)
+    bound, work = kernel_work(dom, w, s)
+    avg_s = per_launch_us[dom] * 1e-6
+    if bound == "mfma":
+        peak = PEAK[w.prec]
+        roof = {"bound": "mfma", "kernel": dom, "achieved": work / avg_s / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": work / avg_s / peak, "traffic": None,
+                "work_per_launch": f"{work:.4g} FLOP", "avg_launch_us": per_launch_us[dom]}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": work / avg_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": work / avg_s / HBM_PEAK, "traffic": None,
+                "work_per_launch": f"{work:.4g} B", "avg_launch_us": per_launch_us[dom]}
+    memk = {}
+    for name in ("dispatch", "combine", "combine_bwd", "dispatch_bwd"):
+        if name in per_launch_us:
+            _, b = kernel_work(name, w, s)
+            memk[name] = round(b / (per_launch_us[name] * 1e-6) / 1e9, 1)
+
+    line = {
+        "metric": METRIC,
+        "value": w.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8"}[w.prec],
+        "data": "synthetic: seeded normal activations/logits/upstream grads, random-init weights (std 0.02)",
+        "config": {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f}, SwiGLU experts, "
+                               f"fwd+bwd incl. routing", "global_batch": w.T, "parallelism": "single GPU"},
+        "roofline": roof,
+        "gemm": {"tflops": gemm_tflops, "frac_of_peak": (gemm_tflops * 1e12 / PEAK[w.prec]) if gemm_tflops else None,
+                 "flops_per_step": gemm_flops, "us_per_step": gemm_us},
+        "hbm_kernels_gbps": memk,
+        "kernels_us_per_step": {k: round(v, 2) for k, v in sorted(per_step_us.items())},
+        "peak_mem_gib": peak_mem / 2**30,
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

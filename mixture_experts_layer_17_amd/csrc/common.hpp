@@ -1,0 +1,127 @@
+// Internal helpers shared by the libmoe HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// bf16 stored as raw uint16 bits; conversions are explicit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest, ties to even (finite inputs; NaN handling unspecified).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Element type traits for the two storage types of the data-movement kernels.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ void unpack(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float* o) {
+    return make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                      __float_as_uint(o[3]));
+  }
+  __device__ static __forceinline__ float load1(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static __forceinline__ uint4 pack(const float* o) {
+    return make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                      pack_bf16x2(o[6], o[7]));
+  }
+  __device__ static __forceinline__ float load1(const void* p, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
+  }
+};
+
+// Wave-wide sum (64 lanes), result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Launch wrapper: optionally brackets each launch with timing events (timing.hip).
+// ---------------------------------------------------------------------------
+bool timing_on();
+void timing_mark(const char* name, hipStream_t s, bool begin);
+
+#define MOE_LAUNCH(name, kernel, grid, block, shmem, stream, ...)             \
+  do {                                                                        \
+    const bool moe_t_ = ::moe::timing_on();                                   \
+    if (moe_t_) ::moe::timing_mark(name, stream, true);                       \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);      \
+    if (moe_t_) ::moe::timing_mark(name, stream, false);                      \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// Host-side helpers.
+// ---------------------------------------------------------------------------
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Zero-fill with a kernel (never hipMemsetAsync, so that callers may capture
+// the calls in a HIP graph).  Each translation unit gets its own copy.
+namespace {
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint8_t* __restrict__ p, size_t bytes) {
+  const size_t n16 = bytes / 16;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n16) reinterpret_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
+  const size_t tail = bytes - n16 * 16;
+  if (i < tail) p[n16 * 16 + i] = 0;
+}
+inline void launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return;
+  const size_t n = bytes / 16 > 16 ? bytes / 16 : 16;
+  MOE_LAUNCH("zero_fill", zero_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<uint8_t*>(p), bytes);
+}
+}  // namespace
+
+// Largest supported sizes.
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+
+}  // namespace moe

@@ -1,0 +1,189 @@
+// Host entry points of the grouped SwiGLU expert FFN, the device tile table,
+// and the library's version / status helpers.
+//
+// Olmo-core 3 announcement, "Scaling and optimizing MoE training": the expert
+// products run as one grouped computation, and the routing metadata stays on
+// the GPU.  The host therefore sizes every launch from host-known bounds
+// (R, E, d, f) only; a one-workgroup kernel turns the device offsets into a
+// table of BM-row tiles, and each GEMM workgroup reads its tile from it.
+#include "ffn_common.hpp"
+#include "mx_common.hpp"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets, int E, int BM,
+                                                       int64_t R, int64_t max_tiles, int4* __restrict__ tiles) {
+  __shared__ int64_t start[kMaxE + 1];
+  const int tid = threadIdx.x;
+  int n = 0;
+  int64_t off = 0;
+  if (tid < E) {
+    off = offsets[tid];
+    n = offsets[tid + 1] - offsets[tid];
+    if (n < 0) n = 0;
+    start[tid + 1] = (n + BM - 1) / BM;
+  }
+  if (tid == 0) start[0] = 0;
+  __syncthreads();
+  if (tid == 0)
+    for (int e = 0; e < E; ++e) start[e + 1] += start[e];
+  __syncthreads();
+  if (tid < E) {
+    const int64_t nt = start[tid + 1] - start[tid];
+    for (int64_t i = 0; i < nt; ++i) {
+      const int64_t slot = start[tid] + i;
+      if (slot >= max_tiles) break;
+      const int64_t r0 = off + i * BM;
+      int64_t rows = n - i * BM < BM ? n - i * BM : BM;
+      if (r0 + rows > R) rows = R - r0 > 0 ? R - r0 : 0;  // memory safety against bad offsets
+      tiles[slot] = make_int4(rows > 0 ? tid : -1, static_cast<int>(r0), static_cast<int>(rows), 0);
+    }
+  }
+  const int64_t used = start[E] < max_tiles ? start[E] : max_tiles;
+  for (int64_t i = used + tid; i < max_tiles; i += blockDim.x) tiles[i] = make_int4(-1, 0, 0, 0);
+}
+
+struct FfnShape {
+  int64_t R;
+  int E, d, f, prec;
+};
+
+bool shape_ok(const FfnShape& s) {
+  if (s.R < 0 || s.R >= (1ll << 31) || s.E < 1 || s.E > kMaxE || s.d <= 0 || s.f <= 0) return false;
+  if (s.prec != MOE_F32 && s.prec != MOE_BF16 && s.prec != MOE_MXFP8) return false;
+  return true;
+}
+
+bool shape_supported(const FfnShape& s) {
+  const int q = s.prec == MOE_MXFP8 ? 128 : 64;
+  return s.d % q == 0 && s.f % q == 0;
+}
+
+int tile_bm(int prec) { return prec == MOE_F32 ? ffn_f32_bm() : ffn_bf16_bm(); }
+
+size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }
+
+// Workspace layout: [tile table][dHg][dHu] (backward only) [MX scratch] (MXFP8 only).
+size_t tiles_bytes(const FfnShape& s) {
+  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec))) * sizeof(int4), 256);
+}
+
+size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {
+  size_t b = tiles_bytes(s);
+  if (is_bwd) b += 2 * align_up(static_cast<size_t>(s.R) * s.f * elem_bytes(s.prec), 256);
+  if (s.prec == MOE_MXFP8) b += mx_ffn_scratch_bytes(s.R, s.E, s.d, s.f, is_bwd);
+  return b;
+}
+
+}  // namespace
+
+void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
+                     hipStream_t s) {
+  MOE_LAUNCH("tile_map", tile_map_kernel, dim3(1), dim3(256), 0, s, offsets, E, BM, R, max_tiles, tiles);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_abi_version(void) { return 1; }
+
+extern "C" const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or type";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+extern "C" size_t moe_grouped_ffn_workspace(int64_t R, int32_t E, int32_t d, int32_t f, int prec, int is_bwd) {
+  const FfnShape s{R, E, d, f, prec};
+  if (!shape_ok(s)) return 0;
+  return ffn_ws_bytes(s, is_bwd);
+}
+
+extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
+                                   const void* x_perm, const void* w_gate, const void* w_up, const void* w_down,
+                                   void* h_gate, void* h_up, void* a_act, void* y_perm, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  const FfnShape sh{R, E, d, f, prec};
+  if (!shape_ok(sh)) return MOE_EINVAL;
+  if (!shape_supported(sh)) return MOE_EUNSUPPORTED;
+  if (!offsets || !w_gate || !w_up || !w_down || !ws) return MOE_EINVAL;
+  if (R > 0 && (!x_perm || !h_gate || !h_up || !a_act || !y_perm)) return MOE_EINVAL;
+  for (const void* p : {x_perm, w_gate, w_up, w_down, (const void*)h_gate, (const void*)h_up, (const void*)a_act,
+                        (const void*)y_perm, (const void*)ws})
+    if (p && !aligned16(p)) return MOE_EINVAL;
+  if (ws_bytes < ffn_ws_bytes(sh, 0)) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (R == 0) return MOE_OK;
+  const int bm = tile_bm(prec);
+  const int64_t mt = max_m_tiles(R, E, bm);
+  int4* tiles = static_cast<int4*>(ws);
+  launch_tile_map(offsets, E, bm, R, mt, tiles, s);
+  FfnArgs a{};
+  a.offsets = offsets;
+  a.tiles = tiles;
+  a.E = E; a.d = d; a.f = f; a.R = R;
+  a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
+  a.o_hg = h_gate; a.o_hu = h_up; a.o_act = a_act; a.act = a_act; a.o_y = y_perm;
+  if (prec == MOE_MXFP8) {
+    char* mxs = static_cast<char*>(ws) + tiles_bytes(sh);
+    return mx_ffn_fwd(a, mt, mxs, s);
+  }
+  auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
+  int st = launch(kG1, a, mt, s);
+  if (st == MOE_OK) st = launch(kG2, a, mt, s);
+  return st;
+}
+
+extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
+                                   const int32_t* mx_blk_offsets, const void* dy_perm, const void* x_perm,
+                                   const void* h_gate, const void* h_up, const void* a_act, const void* w_gate,
+                                   const void* w_up, const void* w_down, void* dx_perm, void* dw_gate, void* dw_up,
+                                   void* dw_down, void* ws, size_t ws_bytes, void* stream) {
+  const FfnShape sh{R, E, d, f, prec};
+  if (!shape_ok(sh)) return MOE_EINVAL;
+  if (!shape_supported(sh)) return MOE_EUNSUPPORTED;
+  if (!offsets || !w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down || !ws) return MOE_EINVAL;
+  if (R > 0 && (!dy_perm || !x_perm || !h_gate || !h_up || !a_act || !dx_perm)) return MOE_EINVAL;
+  if (prec == MOE_MXFP8 && !mx_blk_offsets) return MOE_EINVAL;
+  for (const void* p : {dy_perm, x_perm, h_gate, h_up, a_act, w_gate, w_up, w_down, (const void*)dx_perm,
+                        (const void*)dw_gate, (const void*)dw_up, (const void*)dw_down, (const void*)ws})
+    if (p && !aligned16(p)) return MOE_EINVAL;
+  if (ws_bytes < ffn_ws_bytes(sh, 1)) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bm = tile_bm(prec);
+  const int64_t mt = max_m_tiles(R, E, bm);
+  char* wsb = static_cast<char*>(ws);
+  int4* tiles = reinterpret_cast<int4*>(wsb);
+  const size_t hbytes = align_up(static_cast<size_t>(R) * f * elem_bytes(prec), 256);
+  void* dhg = wsb + tiles_bytes(sh);
+  void* dhu = wsb + tiles_bytes(sh) + hbytes;
+  launch_tile_map(offsets, E, bm, R, mt, tiles, s);
+  FfnArgs a{};
+  a.offsets = offsets;
+  a.tiles = tiles;
+  a.E = E; a.d = d; a.f = f; a.R = R;
+  a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
+  a.hg = h_gate; a.hu = h_up; a.act = a_act; a.dy = dy_perm;
+  a.o_dhg = dhg; a.o_dhu = dhu; a.dhg = dhg; a.dhu = dhu;
+  a.o_dx = dx_perm; a.o_dwg = dw_gate; a.o_dwu = dw_up; a.o_dwd = dw_down;
+  if (prec == MOE_MXFP8) {
+    char* mxs = wsb + tiles_bytes(sh) + 2 * hbytes;
+    return mx_ffn_bwd(a, mt, mx_blk_offsets, mxs, s);
+  }
+  auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
+  int st = MOE_OK;
+  if (R > 0) {
+    st = launch(kG3, a, mt, s);
+    if (st == MOE_OK) st = launch(kG5, a, mt, s);
+  }
+  if (st == MOE_OK) st = launch(kG4, a, mt, s);
+  if (st == MOE_OK) st = launch(kG6, a, mt, s);
+  return st;
+}

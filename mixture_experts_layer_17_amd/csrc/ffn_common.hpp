@@ -1,0 +1,48 @@
+// Shared definitions of the grouped expert-FFN GEMMs (internal).
+//
+// The six products of one SwiGLU expert FFN, forward and backward, run as
+// grouped GEMMs over the expert-major buffer (Olmo-core 3 announcement,
+// "Scaling and optimizing MoE training": the many small expert products become
+// one grouped computation):
+//   G1  [Hg | Hu] = X Wg_e | X Wu_e, epilogue A = silu(Hg) * Hu   rows by expert
+//   G2  Y = A Wd_e                                                rows by expert
+//   G3  dA = dY Wd_e^T, epilogue dHg, dHu (SwiGLU backward)        rows by expert
+//   G4  dWd_e = A_e^T dY_e                                        K = rows of e
+//   G5  dX = dHg Wg_e^T + dHu Wu_e^T                              rows by expert
+//   G6  dWg_e = X_e^T dHg_e, dWu_e = X_e^T dHu_e                  K = rows of e
+// "Rows by expert" GEMMs walk a device-built tile table (one entry per
+// BM-row tile of each expert segment), so the grid size is a host-known bound
+// and the host never reads the routing counts.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+enum FfnKind { kG1 = 1, kG2 = 2, kG3 = 3, kG4 = 4, kG5 = 5, kG6 = 6 };
+
+struct FfnArgs {
+  const int32_t* offsets;  // [E+1] expert segment offsets (device)
+  const int4* tiles;       // M-tile table: {expert, row0, rows, 0}; expert < 0 past the end
+  int E, d, f;
+  int64_t R;
+  // inputs
+  const void *x, *wg, *wu, *wd, *hg, *hu, *act, *dy, *dhg, *dhu;
+  // outputs
+  void *o_hg, *o_hu, *o_act, *o_y, *o_dhg, *o_dhu, *o_dx, *o_dwg, *o_dwu, *o_dwd;
+};
+
+// Upper bound of BM-row tiles over all expert segments: sum ceil(n_e / BM).
+inline int64_t max_m_tiles(int64_t R, int E, int BM) { return cdiv(R, BM) + E; }
+
+// Launch the tile-table builder (defined in ffn.hip).
+void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
+                     hipStream_t s);
+
+// GEMM launchers (defined in gemm_bf16.hip / gemm_f32.hip).
+int launch_ffn_bf16(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s);
+int launch_ffn_f32(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s);
+int ffn_bf16_bm();
+int ffn_f32_bm();
+
+}  // namespace moe

@@ -1,0 +1,65 @@
+// MXFP8 internals shared by the quantiser, the MX GEMMs and the FFN entry points.
+#pragma once
+
+#include "ffn_common.hpp"
+
+namespace moe {
+
+// E4M3 encoding of one fp32 value: round to nearest, ties to even, saturated to
+// +-448, sign kept.  Integer arithmetic on the fp32 bit pattern, so the result
+// is exact for every finite input.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {  // |y| >= 448: anything that rounds past 448 saturates
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {  // |y| >= 2^-6: normal E4M3; drop 20 mantissa bits with RNE
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);  // rebias the exponent 127 -> 7
+  } else {  // subnormal E4M3: multiples of 2^-9, RNE to an integer (8 becomes 2^-6 = 0x08)
+    code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  }
+  return code | sign;
+}
+
+// Shared block exponent e = floor(log2(amax)) - 8, clamped to [-127, 127];
+// -127 for an all-zero block.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
+  int p;
+  if (b >= 0x00800000u) {
+    p = static_cast<int>(b >> 23) - 127;
+  } else if (b != 0u) {
+    p = (31 - __clz(static_cast<int>(b))) - 149;  // fp32 subnormal
+  } else {
+    return -127;
+  }
+  const int e = p - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^-e as an fp32 multiplier (e in [-127, 127]); exact for e >= -126 and for the
+// values that can occur in a block with e = -127 (their scaled magnitudes stay
+// below 2).
+__device__ __forceinline__ float mx_inv_scale(int e) {
+  const int n = -e;  // in [-127, 127]
+  return n >= -126 ? __uint_as_float(static_cast<uint32_t>(n + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Launchers of the quantiser (mx.hip).
+//  rows layout: blocks along the contiguous axis; q [rows, cols], sc [rows, cols/32]
+void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sc,
+                    hipStream_t s);
+//  column layout: blocks run down the rows, stored transposed: q [batch][cols][ldq], sc [batch][cols][ldq/32].
+//  With seg (device, nseg+1 offsets; batch 1) blocks restart at each segment.
+void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
+                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s);
+
+// MXFP8 expert FFN (gemm_mx.hip).
+size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd);
+int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, char* scratch, hipStream_t s);
+int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, char* scratch, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,219 @@
+// Row-wise dispatch into the expert-major buffer and the weighted combine, with
+// their backward passes.
+//
+// Olmo-core 3 announcement, "Scaling and optimizing MoE training": routed data
+// is written directly into the experts' input buffers, keeping the reordering
+// work minimal; the gains of MXFP8 came mostly from the expert FFN and from
+// moving data between experts, so these kernels are pure HBM streams.
+//
+// All four kernels are token-major: one wave owns one token, so each token row
+// is read (or written) exactly once and the k expert-buffer rows it touches are
+// whole 16-byte-vector rows.  Every access is a 16-byte vector, 1 KiB per wave
+// instruction.  The k row indices of a token are wave-uniform scalar loads.
+// Sums run in fp32 in slot order j = 0..k-1.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;       // tokens per workgroup
+constexpr int kMaxChunks = 16;  // 16-byte vectors per lane held in registers (d <= 8192 bf16)
+
+template <typename T>
+__global__ __launch_bounds__(64 * kWaves) void dispatch_kernel(const T* __restrict__ x, int64_t Tn, int d, int k,
+                                                              const int32_t* __restrict__ perm_dst,
+                                                              T* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int nvec = d / Elem<T>::kVec;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+  int rows[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) rows[j] = j < k ? perm_dst[t * k + j] : 0;
+  for (int c0 = 0; c0 < nvec; c0 += 64 * kMaxChunks) {
+    uint4 v[kMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = c0 + i * 64 + lane;
+      if (c < nvec) v[i] = src[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      uint4* dst = reinterpret_cast<uint4*>(x_perm + static_cast<int64_t>(rows[j]) * d);
+#pragma unroll
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = c0 + i * 64 + lane;
+        if (c < nvec) dst[c] = v[i];
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64 * kWaves) void gather_sum_kernel(const T* __restrict__ src_rows, int64_t Tn, int d,
+                                                                int k, const int32_t* __restrict__ perm_dst,
+                                                                const float* __restrict__ gates,
+                                                                T* __restrict__ out) {
+  // out[t] = sum_j w_j * src_rows[perm_dst[t*k+j]], w_j = gates[t,j] or 1 (gates == nullptr)
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int nvec = d / V;
+  int rows[kMaxK];
+  float w[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rows[j] = j < k ? perm_dst[t * k + j] : 0;
+    w[j] = j < k ? (gates ? gates[t * k + j] : 1.0f) : 0.f;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + t * d);
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    uint4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) v[j] = reinterpret_cast<const uint4*>(src_rows + static_cast<int64_t>(rows[j]) * d)[c];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        float f[V];
+        Elem<T>::unpack(v[j], f);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += w[j] * f[i];
+      }
+    }
+    dst[c] = Elem<T>::pack(acc);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64 * kWaves) void combine_bwd_kernel(const T* __restrict__ dout,
+                                                                 const T* __restrict__ y_perm, int64_t Tn, int d,
+                                                                 int k, const int32_t* __restrict__ perm_dst,
+                                                                 const float* __restrict__ gates,
+                                                                 T* __restrict__ dy_perm, float* __restrict__ dgates) {
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int nvec = d / V;
+  int rows[kMaxK];
+  float g[kMaxK], dot[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rows[j] = j < k ? perm_dst[t * k + j] : 0;
+    g[j] = j < k ? gates[t * k + j] : 0.f;
+    dot[j] = 0.f;
+  }
+  const uint4* src = reinterpret_cast<const uint4*>(dout + t * d);
+  for (int c = lane; c < nvec; c += 64) {
+    float o[V];
+    Elem<T>::unpack(src[c], o);
+    uint4 yv[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) yv[j] = reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[c];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        float y[V], s[V];
+        Elem<T>::unpack(yv[j], y);
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) { p += o[i] * y[i]; s[i] = g[j] * o[i]; }
+        dot[j] += p;
+        reinterpret_cast<uint4*>(dy_perm + static_cast<int64_t>(rows[j]) * d)[c] = Elem<T>::pack(s);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      const float s = wave_sum(dot[j]);
+      if (lane == 0) dgates[t * k + j] = s;
+    }
+  }
+}
+
+bool dims_ok(int dtype, int64_t T, int d, int k) {
+  return (dtype == MOE_F32 || dtype == MOE_BF16) && T >= 0 && d > 0 && d % 8 == 0 && k >= 1 && k <= kMaxK &&
+         T * k < (1ll << 31) && static_cast<int64_t>(d) * (T * k) < (1ll << 62);
+}
+
+inline dim3 grid_for(int64_t T) { return dim3(static_cast<unsigned>(cdiv(T, kWaves))); }
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_dispatch(const void* x, int dtype, int64_t T, int32_t d, int32_t k, const int32_t* perm_dst,
+                            void* x_perm, void* stream) {
+  if (!dims_ok(dtype, T, d, k)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !perm_dst || !x_perm || !aligned16(x) || !aligned16(x_perm)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MOE_F32)
+    MOE_LAUNCH("dispatch", dispatch_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s, static_cast<const float*>(x), T,
+                       d, k, perm_dst, static_cast<float*>(x_perm));
+  else
+    MOE_LAUNCH("dispatch", dispatch_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const uint16_t*>(x), T, d, k, perm_dst, static_cast<uint16_t*>(x_perm));
+  return launch_status();
+}
+
+extern "C" int moe_dispatch_bwd(const void* dx_perm, int dtype, int64_t T, int32_t d, int32_t k,
+                                const int32_t* perm_dst, void* dx, void* stream) {
+  if (!dims_ok(dtype, T, d, k)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!dx_perm || !perm_dst || !dx || !aligned16(dx_perm) || !aligned16(dx)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MOE_F32)
+    MOE_LAUNCH("dispatch_bwd", gather_sum_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const float*>(dx_perm), T, d, k, perm_dst, nullptr, static_cast<float*>(dx));
+  else
+    MOE_LAUNCH("dispatch_bwd", gather_sum_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const uint16_t*>(dx_perm), T, d, k, perm_dst, nullptr,
+                       static_cast<uint16_t*>(dx));
+  return launch_status();
+}
+
+extern "C" int moe_combine(const void* y_perm, int dtype, const float* gates, const int32_t* perm_dst, int64_t T,
+                           int32_t d, int32_t k, void* out, void* stream) {
+  if (!dims_ok(dtype, T, d, k)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !gates || !perm_dst || !out || !aligned16(y_perm) || !aligned16(out)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MOE_F32)
+    MOE_LAUNCH("combine", gather_sum_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const float*>(y_perm), T, d, k, perm_dst, gates, static_cast<float*>(out));
+  else
+    MOE_LAUNCH("combine", gather_sum_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst, gates, static_cast<uint16_t*>(out));
+  return launch_status();
+}
+
+extern "C" int moe_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* gates,
+                               const int32_t* perm_dst, int64_t T, int32_t d, int32_t k, void* dy_perm,
+                               float* dgates, void* stream) {
+  if (!dims_ok(dtype, T, d, k)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!dout || !y_perm || !gates || !perm_dst || !dy_perm || !dgates || !aligned16(dout) || !aligned16(y_perm) ||
+      !aligned16(dy_perm))
+    return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MOE_F32)
+    MOE_LAUNCH("combine_bwd", combine_bwd_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const float*>(dout), static_cast<const float*>(y_perm), T, d, k, perm_dst, gates,
+                       static_cast<float*>(dy_perm), dgates);
+  else
+    MOE_LAUNCH("combine_bwd", combine_bwd_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
+                       static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst,
+                       gates, static_cast<uint16_t*>(dy_perm), dgates);
+  return launch_status();
+}

@@ -1,0 +1,302 @@
+// Top-k routing and device-built routing metadata.
+//
+// Olmo-core 3 announcement, "Scaling and optimizing MoE training": routing
+// metadata stays on the GPU so the host can keep enqueuing work without
+// waiting for it; routed rows go straight into the experts' input buffers.
+// Introduction: a fixed number of experts (four of 8 or 128) per token.
+//
+// Three launches, no host synchronisation and no atomics that decide an order:
+//  1. route_select: one wave per 64 tokens.  The 64 x E logit tile is staged
+//     through LDS with coalesced loads; each lane keeps a sorted top-k list of
+//     its token (logit descending, index ascending), writes indices and
+//     renormalised gates, then ORs its lane bit into a per-expert 64-bit mask.
+//     The rank of a token inside its block for expert e is the popcount of the
+//     mask bits below its lane (token order), and the block's count for e is
+//     the popcount of the whole mask.
+//  2. route_scan: one workgroup turns the [blocks x E] count matrix into
+//     counts, offsets, MX block offsets and per-(block, expert) base rows.
+//  3. route_scatter: row = base[block][e] + rank; writes perm_dst and perm_src.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTokPerBlk = 64;   // tokens per routing block (one wave)
+constexpr int kStageMaxE = 128;  // widest logit row staged through LDS
+constexpr int kScanThreads = 1024;
+
+template <int K>
+__global__ __launch_bounds__(64) void route_select_kernel(const float* __restrict__ logits, int64_t T,
+                                                          int E, int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ gates,
+                                                          int32_t* __restrict__ rank,
+                                                          int32_t* __restrict__ blk_counts) {
+  extern __shared__ float smem[];
+  // For E <= kStageMaxE the [64, E] logit tile is staged through LDS with
+  // coalesced loads (odd row stride: lane-private rows hit distinct banks);
+  // wider rows are read by each lane straight from global memory.
+  const bool stage = E <= kStageMaxE;
+  const int ld = E + 1;
+  float* tile = smem;
+  unsigned long long* mask =
+      reinterpret_cast<unsigned long long*>(smem + (stage ? kTokPerBlk * ld : 0));
+  const int lane = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlk;
+  const int ntok = static_cast<int>(T - t0 < kTokPerBlk ? T - t0 : kTokPerBlk);
+
+  const float* src = logits + t0 * E;
+  if (stage) {
+    const int nel = ntok * E;
+    for (int i = lane; i < nel; i += 64) {
+      const int r = i / E;
+      tile[r * ld + (i - r * E)] = src[i];
+    }
+  }
+  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
+  __syncthreads();
+
+  float val[K];
+  int idx[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) { val[i] = 0.f; idx[i] = i; }
+
+  if (lane < ntok) {
+    const float* row = stage ? tile + lane * ld : src + static_cast<int64_t>(lane) * E;
+    for (int e = 0; e < E; ++e) {
+      const float v = row[e];
+      // Candidate e has a larger index than every entry held, so it goes in
+      // front of an entry only when strictly greater.  The first K experts
+      // fill the list unconditionally; entries are never duplicated, so the
+      // result is K distinct valid experts for any input (NaN included).
+      const bool take = (e < K) || (v > val[K - 1]);
+      if (take) {
+        const int pos = e < K ? e : K - 1;
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+          if (i == pos) { val[i] = v; idx[i] = e; }
+#pragma unroll
+        for (int i = K - 1; i >= 1; --i) {
+          if (i <= pos && val[i] > val[i - 1]) {
+            const float tv = val[i]; val[i] = val[i - 1]; val[i - 1] = tv;
+            const int ti = idx[i]; idx[i] = idx[i - 1]; idx[i - 1] = ti;
+          }
+        }
+      }
+    }
+    // Renormalised gates: softmax over the K chosen logits.
+    float z[K];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) { z[i] = __expf(val[i] - val[0]); s += z[i]; }
+    const float inv = 1.0f / s;
+    const int64_t t = t0 + lane;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      topk_idx[t * K + i] = idx[i];
+      gates[t * K + i] = z[i] * inv;
+      atomicOr(&mask[idx[i]], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (lane < ntok) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int64_t t = t0 + lane;
+#pragma unroll
+    for (int i = 0; i < K; ++i) rank[t * K + i] = __popcll(mask[idx[i]] & below);
+  }
+  int32_t* cnt = blk_counts + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = lane; e < E; e += 64) cnt[e] = __popcll(mask[e]);
+}
+
+// One workgroup.  blk_base has the layout of blk_counts and is written in place.
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __restrict__ blk, int nblk, int E,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ mx_blk_offsets) {
+  __shared__ int32_t part[kScanThreads];
+  __shared__ int32_t tot[kMaxE + 1];
+  __shared__ int32_t mxb[kMaxE + 1];
+  const int tid = threadIdx.x;
+  const int parts = kScanThreads / E;  // >= 4 for E <= 256
+  const int e = tid % E;
+  const int p = tid / E;
+  const bool active = p < parts;
+  const int per = (nblk + parts - 1) / parts;
+  const int b0 = active ? min(nblk, p * per) : 0;
+  const int b1 = active ? min(nblk, b0 + per) : 0;
+  int s = 0;
+  if (active)
+    for (int b = b0; b < b1; ++b) s += blk[static_cast<int64_t>(b) * E + e];
+  part[tid] = s;
+  __syncthreads();
+  if (tid < E) {
+    int acc = 0;
+    for (int q = 0; q < parts; ++q) acc += part[q * E + tid];
+    tot[tid] = acc;
+    mxb[tid] = (acc + 31) / 32;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // E <= 256: a serial exclusive scan is short and exactly ordered.
+    int run = 0, runb = 0;
+    for (int x = 0; x < E; ++x) {
+      const int c = tot[x], cb = mxb[x];
+      tot[x] = run; mxb[x] = runb;
+      run += c; runb += cb;
+    }
+    tot[E] = run; mxb[E] = runb;
+  }
+  __syncthreads();
+  if (tid <= E) {
+    offsets[tid] = tot[tid];
+    if (mx_blk_offsets) mx_blk_offsets[tid] = mxb[tid];
+    if (tid < E) counts[tid] = tot[tid + 1] - tot[tid];
+  }
+  // Base of each part = expert offset + counts of earlier parts.
+  if (active) {
+    int base = tot[e];
+    for (int q = 0; q < p; ++q) base += part[q * E + e];
+    for (int b = b0; b < b1; ++b) {
+      const int64_t i = static_cast<int64_t>(b) * E + e;
+      const int c = blk[i];
+      blk[i] = base;
+      base += c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                            const int32_t* __restrict__ rank,
+                                                            const int32_t* __restrict__ blk_base,
+                                                            int64_t R, int k, int E,
+                                                            int32_t* __restrict__ perm_src,
+                                                            int32_t* __restrict__ perm_dst) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= R) return;
+  const int64_t t = i / k;
+  const int64_t b = t / kTokPerBlk;
+  const int e = topk_idx[i];
+  const int row = blk_base[b * E + e] + rank[i];
+  perm_dst[i] = row;
+  perm_src[row] = static_cast<int32_t>(i);
+}
+
+// dlogits[t, e] = g_j (dg_j - sum_i g_i dg_i) if e = S_j, else 0.
+template <int K>
+__global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict__ gates,
+                                                        const float* __restrict__ dgates,
+                                                        const int32_t* __restrict__ topk_idx, int64_t T,
+                                                        int E, float* __restrict__ dlogits) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= T * E) return;
+  const int64_t t = i / E;
+  const int e = static_cast<int>(i - t * E);
+  float inner = 0.f, mine = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const float g = gates[t * K + j], dg = dgates[t * K + j];
+    inner += g * dg;
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (topk_idx[t * K + j] == e) {
+      const float g = gates[t * K + j], dg = dgates[t * K + j];
+      mine = g * (dg - inner);
+    }
+  }
+  // An unselected expert gets exactly zero.
+  bool sel = false;
+#pragma unroll
+  for (int j = 0; j < K; ++j) sel |= topk_idx[t * K + j] == e;
+  dlogits[i] = sel ? mine : 0.f;
+}
+
+size_t route_ws_bytes(int64_t T, int E, int k) {
+  const int64_t nblk = cdiv(T, kTokPerBlk);
+  return align_up(static_cast<size_t>(T * k) * 4, 256) + align_up(static_cast<size_t>(nblk * E) * 4, 256);
+}
+
+template <int K>
+void launch_select(const float* logits, int64_t T, int E, int32_t* idx, float* gates, int32_t* rank,
+                   int32_t* blk, hipStream_t s) {
+  const int64_t nblk = cdiv(T, kTokPerBlk);
+  const size_t tile = E <= kStageMaxE ? static_cast<size_t>(kTokPerBlk) * (E + 1) * sizeof(float) : 0;
+  const size_t lds = tile + static_cast<size_t>(E) * 8;
+  MOE_LAUNCH("route_select", route_select_kernel<K>, dim3(static_cast<unsigned>(nblk)), dim3(64), lds, s, logits,
+                     T, E, idx, gates, rank, blk);
+}
+
+template <int K>
+void launch_bwd(const float* g, const float* dg, const int32_t* idx, int64_t T, int E, float* dl,
+                hipStream_t s) {
+  const int64_t n = T * E;
+  MOE_LAUNCH("route_topk_bwd", route_bwd_kernel<K>, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, g, dg,
+                     idx, T, E, dl);
+}
+
+bool route_args_ok(int64_t T, int E, int k) {
+  return T >= 0 && E >= 1 && E <= kMaxE && k >= 1 && k <= kMaxK && k <= E && T * k < (1ll << 31);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_route_topk_workspace(int64_t T, int32_t E, int32_t k) {
+  if (!route_args_ok(T, E, k)) return 0;
+  return route_ws_bytes(T, E, k);
+}
+
+extern "C" int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* perm_dst, int32_t* mx_blk_offsets, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!route_args_ok(T, E, k)) return (E > kMaxE || k > kMaxK) ? MOE_EUNSUPPORTED : MOE_EINVAL;
+  if (!counts || !offsets || !ws) return MOE_EINVAL;
+  if (T > 0 && (!logits || !topk_idx || !gates || !perm_src || !perm_dst)) return MOE_EINVAL;
+  if (ws_bytes < route_ws_bytes(T, E, k)) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nblk = cdiv(T, kTokPerBlk);
+  int32_t* rank = static_cast<int32_t*>(ws);
+  int32_t* blk = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(static_cast<size_t>(T * k) * 4, 256));
+  if (T > 0) {
+    switch (k) {
+      case 1: launch_select<1>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      case 2: launch_select<2>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      case 3: launch_select<3>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      case 4: launch_select<4>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      case 5: launch_select<5>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      case 6: launch_select<6>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      case 7: launch_select<7>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+      default: launch_select<8>(logits, T, E, topk_idx, gates, rank, blk, s); break;
+    }
+  }
+  MOE_LAUNCH("route_scan", route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, static_cast<int>(nblk), E,
+                     counts, offsets, mx_blk_offsets);
+  if (T > 0) {
+    const int64_t R = T * k;
+    MOE_LAUNCH("route_scatter", route_scatter_kernel, dim3(static_cast<unsigned>(cdiv(R, 256))), dim3(256), 0, s,
+                       topk_idx, rank, blk, R, k, E, perm_src, perm_dst);
+  }
+  return launch_status();
+}
+
+extern "C" int moe_route_topk_bwd(const float* gates, const float* dgates, const int32_t* topk_idx,
+                                  int64_t T, int32_t E, int32_t k, float* dlogits, void* stream) {
+  if (!route_args_ok(T, E, k)) return (E > kMaxE || k > kMaxK) ? MOE_EUNSUPPORTED : MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!gates || !dgates || !topk_idx || !dlogits) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (k) {
+    case 1: launch_bwd<1>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    case 2: launch_bwd<2>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    case 3: launch_bwd<3>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    case 4: launch_bwd<4>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    case 5: launch_bwd<5>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    case 6: launch_bwd<6>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    case 7: launch_bwd<7>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+    default: launch_bwd<8>(gates, dgates, topk_idx, T, E, dlogits, s); break;
+  }
+  return launch_status();
+}

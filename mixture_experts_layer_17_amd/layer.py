@@ -1,0 +1,105 @@
+"""One MoE layer step (forward + backward) as a sequence of libmoe ABI calls.
+
+Olmo-core 3 announcement, "Scaling and optimizing MoE training": route, place
+the routed rows straight into the experts' buffers, run the expert FFN as a
+grouped GEMM, combine; the routing metadata never leaves the GPU, so the host
+enqueues the whole step without a single synchronisation.
+
+This module only allocates device buffers (once, up front) and calls the
+binding in order; every step runs in libmoe's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .workloads import Workload
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Host inputs (fp32 numpy arrays exactly representable in storage type) -> device tensors."""
+    dt = torch.bfloat16 if inp["storage"] == "bf16" else torch.float32
+    out = {}
+    for key, val in inp.items():
+        if not isinstance(val, np.ndarray):
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(val))
+        out[key] = t.to(device=device, dtype=torch.float32 if key == "logits" else dt)
+    return out
+
+
+class LayerStep:
+    """Preallocated buffers and workspaces for one layer step of workload ``w``."""
+
+    def __init__(self, w: Workload, dev_inputs: dict):
+        self.w = w
+        self.inp = dev_inputs
+        x = dev_inputs["x"]
+        dev = x.device
+        T, d, E, k, f, R = w.T, w.d, w.E, w.k, w.f, w.R
+        dt = x.dtype
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.linear_router = "w_router" in dev_inputs
+        self.logits = (torch.empty((T, E), dtype=torch.float32, device=dev) if self.linear_router
+                       else dev_inputs["logits"])
+        self.route = {
+            "topk_idx": torch.empty((T, k), **i32),
+            "gates": torch.empty((T, k), dtype=torch.float32, device=dev),
+            "counts": torch.empty(E, **i32),
+            "offsets": torch.empty(E + 1, **i32),
+            "perm_src": torch.empty(R, **i32),
+            "perm_dst": torch.empty(R, **i32),
+            "mx_blk_offsets": torch.empty(E + 1, **i32),
+        }
+        self.route_ws = B._ws(B.lib().moe_route_topk_workspace(T, E, k), dev)
+        self.x_perm = torch.empty((R, d), dtype=dt, device=dev)
+        self.ffn = {n: torch.empty((R, f), dtype=dt, device=dev) for n in ("h_gate", "h_up", "a_act")}
+        self.ffn["y_perm"] = torch.empty((R, d), dtype=dt, device=dev)
+        self.ffn_ws_f = B._ws(B.moe_grouped_ffn_workspace(R, E, d, f, w.prec, 0), dev)
+        self.ffn_ws_b = B._ws(B.moe_grouped_ffn_workspace(R, E, d, f, w.prec, 1), dev)
+        self.out = torch.empty((T, d), dtype=dt, device=dev)
+        self.dy_perm = torch.empty((R, d), dtype=dt, device=dev)
+        self.dgates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.grads = {
+            "dx_perm": torch.empty((R, d), dtype=dt, device=dev),
+            "dw_gate": torch.empty_like(dev_inputs["w_gate"]),
+            "dw_up": torch.empty_like(dev_inputs["w_up"]),
+            "dw_down": torch.empty_like(dev_inputs["w_down"]),
+        }
+        self.dx = torch.empty((T, d), dtype=dt, device=dev)
+        self.dlogits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        if self.linear_router:
+            self.dw_router = torch.empty_like(dev_inputs["w_router"])
+            self.router_ws = B._ws(B.lib().moe_router_logits_bwd_workspace(T, d, E), dev)
+
+    # ------------------------------------------------------------------ steps
+    def forward(self):
+        w, inp = self.w, self.inp
+        if self.linear_router:
+            B.moe_router_logits(inp["x"], inp["w_router"], out=self.logits)
+        B.moe_route_topk(self.logits, w.k, out=self.route, ws=self.route_ws)
+        B.moe_dispatch(inp["x"], self.route["perm_dst"], w.k, out=self.x_perm)
+        B.moe_grouped_ffn_fwd(self.x_perm, self.route["offsets"], inp["w_gate"], inp["w_up"], inp["w_down"], w.prec,
+                              out=self.ffn, ws=self.ffn_ws_f)
+        B.moe_combine(self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"], out=self.out)
+        return self.out
+
+    def backward(self, dout=None):
+        w, inp = self.w, self.inp
+        dout = inp["dout"] if dout is None else dout
+        B.moe_combine_bwd(dout, self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"],
+                          dy_perm=self.dy_perm, dgates=self.dgates)
+        B.moe_grouped_ffn_bwd(self.dy_perm, self.x_perm, self.ffn["h_gate"], self.ffn["h_up"], self.ffn["a_act"],
+                              self.route["offsets"], self.route["mx_blk_offsets"], inp["w_gate"], inp["w_up"],
+                              inp["w_down"], w.prec, out=self.grads, ws=self.ffn_ws_b)
+        B.moe_dispatch_bwd(self.grads["dx_perm"], self.route["perm_dst"], w.k, out=self.dx)
+        B.moe_route_topk_bwd(self.route["gates"], self.dgates, self.route["topk_idx"], w.E, out=self.dlogits)
+        if self.linear_router:
+            B.moe_router_logits_bwd(inp["x"], inp["w_router"], self.dlogits, self.dx, accumulate_dx=True,
+                                    dw_r=self.dw_router, ws=self.router_ws)
+        return self.dx
+
+    def step(self):
+        self.forward()
+        self.backward()

@@ -1,0 +1,91 @@
+"""Helpers of the GPU parity tests: run the HIP path, run the oracle, compare.
+
+The HIP side runs through the binding (the C ABI); the oracle side is the fp64
+CPU oracle on the same host inputs.  The two share only the seeded inputs.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from mixture_experts_layer_17_amd import layer as L
+from mixture_experts_layer_17_amd import workloads as wl
+from oracle import moe_oracle as mo
+
+# max|gpu - oracle| / max|oracle| per tensor
+TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 6e-2}
+INT_KEYS = ("topk_idx", "counts", "offsets", "perm_src", "perm_dst", "mx_blk_offsets")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(gpu, ref) -> float:
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    if g.size == 0:
+        return 0.0
+    m = np.abs(r).max()
+    return float(np.abs(g - r).max() / (m if m > 0 else 1.0))
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def run_gpu_step(w: wl.Workload, inp: dict) -> tuple[dict, L.LayerStep]:
+    step = L.LayerStep(w, L.to_device(inp))
+    step.step()
+    torch.cuda.synchronize()
+    res = {k: host(v) for k, v in step.route.items()}
+    res["logits"] = host(step.logits)
+    res["x_perm"] = host(step.x_perm)
+    res.update({k: host(v) for k, v in step.ffn.items()})
+    res["out"] = host(step.out)
+    res["dgates"] = host(step.dgates)
+    res.update({k: host(v) for k, v in step.grads.items()})
+    res["dx"] = host(step.dx)
+    res["dlogits"] = host(step.dlogits)
+    if step.linear_router:
+        res["dw_router"] = host(step.dw_router)
+    return res, step
+
+
+def run_oracle(w: wl.Workload, inp: dict, gpu_logits: np.ndarray) -> dict:
+    """Oracle layer on the same inputs, routing from the GPU's fp32 logits bytes."""
+    return mo.layer_forward_backward(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], inp["dout"], w.k,
+                                     logits=gpu_logits.astype(np.float32), w_router=inp.get("w_router"))
+
+
+def check_layer(w: wl.Workload, gpu: dict, ref: dict, inp: dict):
+    """Bit-exact integers and copy, float tensors within the precision's tolerance."""
+    tol = TOL[w.prec]
+    if "w_router" in inp:
+        # router logits in fp32 against the fp64 definition
+        e = rel_err(gpu["logits"], mo.router_logits(inp["x"], inp["w_router"]))
+        assert e <= 1e-5, ("logits", e)
+    for key in INT_KEYS:
+        np.testing.assert_array_equal(gpu[key], ref[key], err_msg=key)
+    np.testing.assert_array_equal(gpu["x_perm"], ref["x_perm"], err_msg="x_perm")
+    errs = {"gates": rel_err(gpu["gates"], ref["gates"])}
+    assert errs["gates"] <= 1e-5, errs
+    keys = ["out", "dgates", "dx", "dw_gate", "dw_up", "dw_down", "dlogits"]
+    if "w_router" in inp:
+        keys.append("dw_router")
+    for key in keys:
+        errs[key] = rel_err(gpu[key], ref[key])
+    say(f"  {w.name} T={w.T} d={w.d} E={w.E} k={w.k} f={w.f}: " +
+        " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, f"above tolerance {tol}: {bad}"
+    # empty experts get exactly zero weight gradients
+    empty = np.flatnonzero(ref["counts"] == 0)
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        assert np.all(gpu[key][empty] == 0.0), key

@@ -1,0 +1,86 @@
+"""The C-ABI library loads and exports every declared symbol; host-side
+validation and workspace sizing (CPU only: no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_17_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:moe|mx)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe.so not built: run __graft_entry__.build()")
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    decl = declared_functions()
+    assert len(decl) >= 16
+    for name in decl:
+        assert hasattr(L, name), name
+    assert decl == B.exported_symbols()
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    assert L.moe_status_str(0) == b"ok"
+    assert L.moe_status_str(3) == b"workspace too small"
+
+
+def test_workspace_sizes_are_pure_and_checked(L):
+    a = L.moe_route_topk_workspace(16384, 128, 4)
+    assert a == L.moe_route_topk_workspace(16384, 128, 4) and a >= 16384 * 4 * 4
+    assert L.moe_route_topk_workspace(10, 4, 5) == 0          # k > E
+    f = L.moe_grouped_ffn_workspace(65536, 128, 2048, 1024, 1, 0)
+    b = L.moe_grouped_ffn_workspace(65536, 128, 2048, 1024, 1, 1)
+    assert b >= f + 2 * 65536 * 1024 * 2
+    assert L.moe_grouped_ffn_workspace(-1, 128, 2048, 1024, 1, 0) == 0
+
+
+def test_route_topk_validation(L):
+    s = None
+    assert L.moe_route_topk(FAKE, 10, 4, 5, *[FAKE] * 8, 1 << 20, s) == EINVAL       # k > E
+    assert L.moe_route_topk(FAKE, 10, 300, 4, *[FAKE] * 8, 1 << 20, s) == EUNSUP     # E > 256
+    assert L.moe_route_topk(FAKE, 10, 8, 9, *[FAKE] * 8, 1 << 20, s) == EUNSUP       # k > 8
+    assert L.moe_route_topk(None, 10, 8, 2, *[FAKE] * 8, 1 << 20, s) == EINVAL       # null logits
+    assert L.moe_route_topk(FAKE, 10, 8, 2, *[FAKE] * 8, 4, s) == EWS                # workspace too small
+
+
+def test_ffn_validation(L):
+    s = None
+    args = [FAKE] * 9
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1000, 1, *args, FAKE, 1 << 30, s) == EUNSUP   # f % 64
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 7, *args, FAKE, 1 << 30, s) == EINVAL   # bad precision
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *args, FAKE, 16, s) == EWS
+    bargs = [FAKE] * 14
+    assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *bargs, FAKE, 16, s) == EWS
+    bargs_nomx = [FAKE, None] + [FAKE] * 12
+    assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 2, *bargs_nomx, FAKE, 1 << 40, s) == EINVAL
+    unaligned = [FAKE] + [ctypes.c_void_p(0x10008)] + [FAKE] * 7
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *unaligned, FAKE, 1 << 30, s) == EINVAL
+
+
+def test_permute_and_quantiser_validation(L):
+    s = None
+    assert L.moe_dispatch(FAKE, 5, 10, 64, 2, FAKE, FAKE, s) == EINVAL               # bad dtype
+    assert L.moe_dispatch(FAKE, 1, 10, 60, 2, FAKE, FAKE, s) == EINVAL               # d % 8
+    assert L.moe_combine(FAKE, 1, FAKE, FAKE, 10, 64, 9, FAKE, s) == EINVAL          # k > 8
+    assert L.mx_quantize(FAKE, 1, 1, 64, 40, 1, None, 0, FAKE, FAKE, s) == EINVAL     # cols % 32
+    assert L.mx_quantize(FAKE, 1, 1, 40, 64, 0, None, 0, FAKE, FAKE, s) == EINVAL     # rows % 32
+    assert L.mx_quantize(FAKE, 1, 2, 40, 64, 0, FAKE, 3, FAKE, FAKE, s) == EINVAL     # segments need batch 1
+    assert L.moe_router_logits(FAKE, FAKE, 1, 10, 64, 300, FAKE, s) == EINVAL         # E > 256
