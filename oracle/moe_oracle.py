@@ -227,23 +227,24 @@ def combine_backward(dout, y_perm, gates, perm_dst, k):
     return dy, dg
 
 
-def expert_ffn_backward(dy_perm, x_perm, offsets, w_gate, w_up, w_down):
+def expert_ffn_backward(dy_perm, x_perm, offsets, w_gate, w_up, w_down, want_dw=True):
     """Exact backward of the SwiGLU expert FFN, per expert segment (fp64).
 
     With s = sigmoid(Hg):
       dA = dY Wd^T,  dHu = dA * silu(Hg),  dHg = dA * Hu * s * (1 + Hg (1 - s)),
       dX = dHg Wg^T + dHu Wu^T,
       dWd = A^T dY,  dWg = X^T dHg,  dWu = X^T dHu   (zero for empty experts).
-    The forward intermediates are recomputed here from X in fp64.
+    The forward intermediates are recomputed here from X in fp64.  With
+    want_dw=False the weight gradients are skipped (returned as None).
     """
     dY = np.asarray(dy_perm, np.float64)
     X = np.asarray(x_perm, np.float64)
     E, d, f = np.shape(w_gate)
     R = X.shape[0]
     dx = np.zeros((R, d))
-    dwg = np.zeros((E, d, f))
-    dwu = np.zeros((E, d, f))
-    dwd = np.zeros((E, f, d))
+    dwg = np.zeros((E, d, f)) if want_dw else None
+    dwu = np.zeros((E, d, f)) if want_dw else None
+    dwd = np.zeros((E, f, d)) if want_dw else None
     for e in range(E):
         s = slice(int(offsets[e]), int(offsets[e + 1]))
         if s.start == s.stop:
@@ -257,9 +258,10 @@ def expert_ffn_backward(dy_perm, x_perm, offsets, w_gate, w_up, w_down):
         dhu = da * hg * sg
         dhg = da * hu * sg * (1.0 + hg * (1.0 - sg))
         dx[s] = dhg @ Wg.T + dhu @ Wu.T
-        dwd[e] = a.T @ dY[s]
-        dwg[e] = X[s].T @ dhg
-        dwu[e] = X[s].T @ dhu
+        if want_dw:
+            dwd[e] = a.T @ dY[s]
+            dwg[e] = X[s].T @ dhg
+            dwu[e] = X[s].T @ dhu
     return {"dx_perm": dx, "dw_gate": dwg, "dw_up": dwu, "dw_down": dwd}
 
 
@@ -304,7 +306,7 @@ def router_logits_backward(x, w_r, dlogits):
 # ----------------------------------------------------------------------------
 
 
-def layer_forward_backward(x, w_gate, w_up, w_down, dout, k, *, logits=None, w_router=None):
+def layer_forward_backward(x, w_gate, w_up, w_down, dout, k, *, logits=None, w_router=None, want_dw=True):
     """One MoE layer forward and backward, composed from the steps above.
 
     Either ``w_router`` is given (logits = x W_r, router gradient included) or
@@ -312,6 +314,7 @@ def layer_forward_backward(x, w_gate, w_up, w_down, dout, k, *, logits=None, w_r
     both are given, routing uses the given fp32 ``logits`` (so that both sides
     route from the same bytes) while the router gradient still uses w_router.
     Returns a dict with every intermediate and gradient, fp64 except integers.
+    want_dw=False skips the expert weight gradients (per-token checks).
     """
     x = np.asarray(x, np.float64)
     E = np.asarray(w_gate).shape[0]
@@ -339,7 +342,7 @@ def layer_forward_backward(x, w_gate, w_up, w_down, dout, k, *, logits=None, w_r
     dy, dg = combine_backward(dout, fwd["y_perm"], g, meta["perm_dst"], k)
     res["dy_perm"] = dy
     res["dgates"] = dg
-    bwd = expert_ffn_backward(dy, x_perm, meta["offsets"], w_gate, w_up, w_down)
+    bwd = expert_ffn_backward(dy, x_perm, meta["offsets"], w_gate, w_up, w_down, want_dw=want_dw)
     res.update(bwd)
     dx = dispatch_backward(bwd["dx_perm"], meta["perm_dst"], k)
     dl = topk_gates_backward(g, dg, idx, E)

@@ -49,24 +49,27 @@ def e4m3_decode(codes):
     return np.where((ef == 15) & (mf == 7), np.nan, val)
 
 
+_GRID = None
+
+
+def _grid():
+    """The 127 non-negative finite E4M3 values, ascending (codes 0x00..0x7E)."""
+    global _GRID
+    if _GRID is None:
+        _GRID = e4m3_decode(np.arange(0x7F))
+    return _GRID
+
+
 def e4m3_encode(y):
     """Value (fp64, finite) -> E4M3 byte: round to nearest, ties to even, saturating."""
     y = np.asarray(y, np.float64)
     a = np.abs(y)
     _, ex = np.frexp(a)
     # Grid spacing: 2**(floor(log2 a) - 3) in the normal range, 2**-9 below 2**-6.
-    p = np.maximum(ex - 1, -6)
-    quantum = np.ldexp(1.0, p - 3)
-    r = np.round(a / quantum) * quantum  # np.round rounds half to even
-    r = np.minimum(r, E4M3_MAX)
-    _, ex2 = np.frexp(r)
-    p2 = ex2 - 1
-    normal = r >= 2.0 ** -6
-    efield = np.where(normal, p2 + 7, 0)
-    mfield = np.where(normal,
-                      np.round(np.ldexp(r, -p2) * 8.0) - 8.0,
-                      np.round(r / 2.0 ** -9))
-    code = (efield.astype(np.int64) << 3) | mfield.astype(np.int64)
+    quantum = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+    r = np.minimum(np.round(a / quantum) * quantum, E4M3_MAX)  # np.round rounds half to even
+    # r lies exactly on the E4M3 grid; its code is its index among the ascending values
+    code = np.searchsorted(_grid(), r)
     code = np.where(np.signbit(y), code | 0x80, code)
     return code.astype(np.uint8)
 

@@ -37,7 +37,7 @@ def test_combine_uses_wrong_slot_order(monkeypatch):
 
 
 def test_dhg_missing_term(monkeypatch):
-    def bad(dy_perm, x_perm, offsets, wg, wu, wd):
+    def bad(dy_perm, x_perm, offsets, wg, wu, wd, want_dw=True):
         X, dY = np.asarray(x_perm, float), np.asarray(dy_perm, float)
         out = {"dx_perm": np.zeros_like(X), "dw_gate": np.zeros_like(wg), "dw_up": np.zeros_like(wu),
                "dw_down": np.zeros_like(wd)}
@@ -60,8 +60,8 @@ def test_dhg_missing_term(monkeypatch):
 def test_wgrad_operands_swapped(monkeypatch):
     orig = mo.expert_ffn_backward
 
-    def bad(*a):
-        r = orig(*a)
+    def bad(*a, **kw):
+        r = orig(*a, **kw)
         r["dw_gate"], r["dw_up"] = r["dw_up"], r["dw_gate"]
         return r
     monkeypatch.setattr(mo, "expert_ffn_backward", bad)
@@ -141,3 +141,22 @@ def test_e4m3_no_saturation():
         c = mx.e4m3_encode(y).astype(np.int64)
         return np.where(np.abs(y) > 464, c | 0x7F, c).astype(np.uint8)  # NaN instead of 448
     _fails(pins.check_encode, bad)
+
+
+def test_mx_weight_quantised_along_wrong_axis():
+    from oracle import moe_mx_oracle as mxl
+
+    def layer_with_bad_axes(p):
+        inner = mxl.q_along
+
+        def bad(v, axis, seg=None):
+            # weights (the two 64/96-sized operands) encoded along the wrong axis
+            if seg is None and set(np.shape(v)) == {64, 96}:
+                axis = 1 - axis
+            return inner(v, axis, seg)
+        mxl.q_along = bad
+        try:
+            return pins._mx_layer(p)
+        finally:
+            mxl.q_along = inner
+    _fails(pins.check_mx_axes, layer_with_bad_axes)

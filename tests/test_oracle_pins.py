@@ -444,3 +444,99 @@ def test_mx_axis0_segments_restart_and_pad():
             b += 1
     atol = np.exp2(s.astype(np.float64).max() - 127 - 10)
     np.testing.assert_allclose(mx.mx_dequantize(q, s, axis=0, seg_offsets=seg), v, rtol=0.125, atol=atol)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 layer oracle: structure pins
+# ---------------------------------------------------------------------------
+
+def _mx_problem(seed=13, T=40, d=64, E=4, k=2, f=96):
+    p = tiny_problem(seed, T, d, E, k, f, router=False)
+    return p
+
+
+def test_mx_layer_with_identity_encoding_is_the_plain_oracle(monkeypatch):
+    from oracle import moe_mx_oracle as mxl
+    p = _mx_problem()
+    monkeypatch.setattr(mxl, "q_along", lambda v, axis, seg=None: np.asarray(v, np.float64))
+    monkeypatch.setattr(mxl, "round_to_bf16", lambda v: np.asarray(v, np.float64))
+    got = mxl.mx_layer_forward_backward(p["x"], p["w_gate"], p["w_up"], p["w_down"], p["dout"], p["k"],
+                                        logits=p["logits"])
+    ref = oracle_out(p)
+    for key in ("out", "dgates", "dx", "dw_gate", "dw_up", "dw_down", "dlogits", "perm_src"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-12, atol=1e-12, err_msg=key)
+
+
+def mx_quantisation_calls(layer_fn, p):
+    """(shape, axis, segmented) of every MX encoding the layer oracle applies."""
+    from oracle import moe_mx_oracle as mxl
+    calls = []
+    orig = mxl.q_along
+
+    def rec(v, axis, seg=None):
+        calls.append((tuple(np.shape(v)), axis, seg is not None))
+        return orig(v, axis, seg)
+    mxl.q_along = rec
+    try:
+        layer_fn(p)
+    finally:
+        mxl.q_along = orig
+    return calls
+
+
+def check_mx_axes(layer_fn):
+    """Every GEMM operand is encoded along that GEMM's contraction axis (module
+    table), in the order the steps run: forward, input gradients, weight gradients."""
+    p = _mx_problem(T=80, d=64, E=2, k=1, f=96)
+    idx = mo.topk_select(p["logits"], 1)
+    n = np.bincount(idx.ravel(), minlength=2)
+    assert n.min() > 0
+    R, d, f = 80, 64, 96
+    want = [((R, d), 1, False)]                                       # X along d (G1)
+    for e in range(2):
+        want += [((d, f), 0, False), ((d, f), 0, False)]              # Wg_e, Wu_e along d (G1)
+    want += [((R, f), 1, False)]                                      # A along f (G2)
+    want += [((f, d), 0, False)] * 2                                  # Wd_e along f (G2)
+    want += [((R, d), 1, False)]                                      # dY along d (G3)
+    want += [((f, d), 1, False)] * 2                                  # Wd_e along d (G3)
+    want += [((R, f), 1, False), ((R, f), 1, False)]                  # dHg, dHu along f (G5)
+    for e in range(2):
+        ne = int(n[e])
+        want += [((d, f), 1, False), ((d, f), 1, False)]              # Wg_e, Wu_e along f (G5)
+        want += [((ne, d), 0, True), ((ne, f), 0, True), ((ne, d), 0, True),   # X_e, A_e, dY_e along tokens
+                 ((ne, f), 0, True), ((ne, f), 0, True)]              # dHg_e, dHu_e along tokens (G4, G6)
+    got = mx_quantisation_calls(layer_fn, p)
+    assert got == want, (got, want)
+
+
+def _mx_layer(p):
+    from oracle import moe_mx_oracle as mxl
+    return mxl.mx_layer_forward_backward(p["x"], p["w_gate"], p["w_up"], p["w_down"], p["dout"], p["k"],
+                                         logits=p["logits"])
+
+
+def test_mx_layer_quantises_along_contraction_axes():
+    check_mx_axes(_mx_layer)
+
+
+def test_mx_layer_error_is_the_encoding_error():
+    # the MX layer differs from the plain oracle by an amount of the order of the
+    # E4M3 rounding (a few percent), never by O(1)
+    p = _mx_problem(T=200, d=128, E=4, k=2, f=128)
+    got = _mx_layer(p)
+    ref = oracle_out(p)
+    for key in ("out", "dx", "dw_gate", "dw_down"):
+        e = np.abs(got[key] - ref[key]).max() / np.abs(ref[key]).max()
+        assert 1e-4 < e < 0.2, (key, e)
+
+
+def test_round_to_bf16_matches_torch_conversion():
+    import torch
+    from oracle import moe_mx_oracle as mxl
+    r = np.random.default_rng(21)
+    v = np.concatenate([r.standard_normal(200000) * np.exp2(r.integers(-40, 40, 200000)),
+                        [1.00390625, 1.01171875, -1.00390625, 0.0, -0.0, 2.0 ** -130, 3.0 * 2.0 ** -133]])
+    v32 = v.astype(np.float32)
+    ref = torch.from_numpy(v32).to(torch.bfloat16).double().numpy()
+    got = mxl.round_to_bf16(v32.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
