@@ -36,7 +36,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    extra = os.environ.get("MOE_HIPCC_DEFINES", "").split()  # e.g. -DMOE_BIG_TILE=2
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
   }
   const int64_t used = start[E] < max_tiles ? start[E] : max_tiles;
   for (int64_t i = used + tid; i < max_tiles; i += blockDim.x) tiles[i] = make_int4(-1, 0, 0, 0);
+  if (tid == 0) tiles[max_tiles] = make_int4(static_cast<int>(used), 0, 0, 0);
 }
 
 struct FfnShape {
@@ -60,13 +61,15 @@ bool shape_supported(const FfnShape& s) {
   return s.d % q == 0 && s.f % q == 0;
 }
 
-int tile_bm(int prec) { return prec == MOE_F32 ? ffn_f32_bm() : ffn_bf16_bm(); }
+int tile_bm(int prec, int64_t R, int E) {
+  return prec == MOE_F32 ? ffn_f32_bm() : prec == MOE_MXFP8 ? 128 : ffn_bf16_bm(R, E);
+}
 
 size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }
 
 // Workspace layout: [tile table][dHg][dHu] (backward only) [MX scratch] (MXFP8 only).
 size_t tiles_bytes(const FfnShape& s) {
-  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec))) * sizeof(int4), 256);
+  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec, s.R, s.E)) + 1) * sizeof(int4), 256);
 }
 
 size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {
@@ -121,13 +124,14 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   if (ws_bytes < ffn_ws_bytes(sh, 0)) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (R == 0) return MOE_OK;
-  const int bm = tile_bm(prec);
+  const int bm = tile_bm(prec, R, E);
   const int64_t mt = max_m_tiles(R, E, bm);
   int4* tiles = static_cast<int4*>(ws);
   launch_tile_map(offsets, E, bm, R, mt, tiles, s);
   FfnArgs a{};
   a.offsets = offsets;
   a.tiles = tiles;
+  a.max_tiles = mt;
   a.E = E; a.d = d; a.f = f; a.R = R;
   a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
   a.o_hg = h_gate; a.o_hu = h_up; a.o_act = a_act; a.act = a_act; a.o_y = y_perm;
@@ -157,7 +161,7 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
     if (p && !aligned16(p)) return MOE_EINVAL;
   if (ws_bytes < ffn_ws_bytes(sh, 1)) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int bm = tile_bm(prec);
+  const int bm = tile_bm(prec, R, E);
   const int64_t mt = max_m_tiles(R, E, bm);
   char* wsb = static_cast<char*>(ws);
   int4* tiles = reinterpret_cast<int4*>(wsb);
@@ -168,6 +172,7 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   FfnArgs a{};
   a.offsets = offsets;
   a.tiles = tiles;
+  a.max_tiles = mt;
   a.E = E; a.d = d; a.f = f; a.R = R;
   a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
   a.hg = h_gate; a.hu = h_up; a.act = a_act; a.dy = dy_perm;

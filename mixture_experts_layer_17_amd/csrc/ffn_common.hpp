@@ -23,7 +23,9 @@ enum FfnKind { kG1 = 1, kG2 = 2, kG3 = 3, kG4 = 4, kG5 = 5, kG6 = 6 };
 
 struct FfnArgs {
   const int32_t* offsets;  // [E+1] expert segment offsets (device)
-  const int4* tiles;       // M-tile table: {expert, row0, rows, 0}; expert < 0 past the end
+  const int4* tiles;       // M-tile table: {expert, row0, rows, 0}; expert < 0 past the end;
+                           // entry [max_tiles] = {number of live tiles, 0, 0, 0}
+  int64_t max_tiles;
   int E, d, f;
   int64_t R;
   // inputs
@@ -35,6 +37,22 @@ struct FfnArgs {
 // Upper bound of BM-row tiles over all expert segments: sum ceil(n_e / BM).
 inline int64_t max_m_tiles(int64_t R, int E, int BM) { return cdiv(R, BM) + E; }
 
+// XCD-aware tile order.  The hardware deals consecutive workgroup ids round-robin
+// over the 8 XCDs (each with its own L2); giving XCD x the contiguous logical
+// range [x*per, (x+1)*per) keeps the tiles that share operands (the N-tiles of
+// one row block, the row blocks of one expert) on one L2.  Returns -1 for
+// workgroups with no tile.  Launch grids are rounded up to a multiple of 8.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t hw_id, int64_t total) {
+  const int64_t per = (total + kNumXcd - 1) / kNumXcd;
+  if (hw_id >= per * kNumXcd) return -1;
+  const int64_t lid = (hw_id % kNumXcd) * per + hw_id / kNumXcd;
+  return lid < total ? lid : -1;
+}
+inline unsigned xcd_grid(int64_t total) {
+  return static_cast<unsigned>(cdiv(total, kNumXcd) * kNumXcd);
+}
+
 // Launch the tile-table builder (defined in ffn.hip).
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
                      hipStream_t s);
@@ -42,7 +60,7 @@ void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t m
 // GEMM launchers (defined in gemm_bf16.hip / gemm_f32.hip).
 int launch_ffn_bf16(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s);
 int launch_ffn_f32(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s);
-int ffn_bf16_bm();
+int ffn_bf16_bm(int64_t R, int E);  // row-tile height for this workload
 int ffn_f32_bm();
 
 }  // namespace moe

@@ -13,15 +13,19 @@
 namespace moe {
 namespace {
 
-constexpr int kChunk = 64;        // tokens per dW_r partial
+constexpr int kChunk = 32;        // tokens per dW_r partial
 constexpr int kTokPerBlk = 32;    // tokens per workgroup in the wave-per-token kernels
 constexpr size_t kMaxLdsW = 64 * 1024;
 
-// Row i of W_r [d, E] widened to fp32 from LDS (EP >= E experts, zero padded).
+// Row i of W_r [d, E] widened to fp32 from LDS (EP >= E experts, zero padded),
+// read as 16-byte vectors (EP * sizeof(T) is a multiple of 16).
 template <typename T, int EP>
 __device__ __forceinline__ void w_row(const T* __restrict__ wl, int i, float* o) {
+  constexpr int V = Elem<T>::kVec;
+  static_assert(EP % V == 0, "W_r rows must be whole 16-byte vectors");
+  const uint4* r = reinterpret_cast<const uint4*>(wl + static_cast<int64_t>(i) * EP);
 #pragma unroll
-  for (int e = 0; e < EP; ++e) o[e] = Elem<T>::load1(wl, static_cast<int64_t>(i) * EP + e);
+  for (int q = 0; q < EP / V; ++q) Elem<T>::unpack(r[q], o + q * V);
 }
 
 template <typename T, int EP>
@@ -218,8 +222,17 @@ __global__ __launch_bounds__(256) void router_bwd_dw_reduce_kernel(const float* 
                                                                   int64_t n, T* __restrict__ dw) {
   const int64_t gi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gi >= n) return;
+  // fixed chunk order; eight loads in flight per step
   float acc = 0.f;
-  for (int c = 0; c < nchunk; ++c) acc += part[c * n + gi];
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = part[(c + q) * n + gi];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += v[q];
+  }
+  for (; c < nchunk; ++c) acc += part[c * n + gi];
   Elem<T>::store1(dw, gi, acc);
 }
 

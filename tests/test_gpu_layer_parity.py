@@ -31,6 +31,9 @@ SMALL = {
     "bf16-single-expert": wl.scaled(W[3], T=130, d=128, f=128, E=1, k=1),
     "bf16-k-equals-E": wl.scaled(W[3], T=96, d=128, f=128, E=8, k=8),
     "bf16-e256-k8": wl.scaled(W[3], T=300, d=128, f=64, E=256, k=8),
+    # >= 1024 rows per expert and d, f multiples of 256: the 256 x 256 tile path
+    "bf16-big-tiles": wl.scaled(W[3], T=2300, d=512, f=256, E=2, k=1),
+    "bf16-big-tiles-k2": wl.scaled(W[3], T=2100, d=256, f=512, E=4, k=2),
     "mxfp8-e16": wl.scaled(W[5], T=700, d=256, f=384, E=16),
     "mxfp8-e128": wl.scaled(W[5], T=1536, d=256, f=256),
 }
