@@ -14,34 +14,49 @@ namespace {
 
 __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets, int E, int BM,
                                                        int64_t R, int64_t max_tiles, int4* __restrict__ tiles) {
-  __shared__ int64_t start[kMaxE + 1];
+  // tile counts per expert, their inclusive prefix sum (Hillis-Steele over
+  // kMaxE = 256 entries), then one thread per table slot
+  __shared__ int64_t cum[kMaxE];
+  __shared__ int32_t off_s[kMaxE], n_s[kMaxE];
+  static_assert(kMaxE == 256, "one thread per expert");
   const int tid = threadIdx.x;
-  int n = 0;
-  int64_t off = 0;
+  int64_t cnt = 0;
   if (tid < E) {
-    off = offsets[tid];
-    n = offsets[tid + 1] - offsets[tid];
+    const int32_t o = offsets[tid];
+    int32_t n = offsets[tid + 1] - o;
     if (n < 0) n = 0;
-    start[tid + 1] = (n + BM - 1) / BM;
+    off_s[tid] = o;
+    n_s[tid] = n;
+    cnt = (n + BM - 1) / BM;
   }
-  if (tid == 0) start[0] = 0;
+  cum[tid] = cnt;
   __syncthreads();
-  if (tid == 0)
-    for (int e = 0; e < E; ++e) start[e + 1] += start[e];
-  __syncthreads();
-  if (tid < E) {
-    const int64_t nt = start[tid + 1] - start[tid];
-    for (int64_t i = 0; i < nt; ++i) {
-      const int64_t slot = start[tid] + i;
-      if (slot >= max_tiles) break;
-      const int64_t r0 = off + i * BM;
-      int64_t rows = n - i * BM < BM ? n - i * BM : BM;
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    const int64_t v = tid >= o ? cum[tid - o] : 0;
+    __syncthreads();
+    cum[tid] += v;
+    __syncthreads();
+  }
+  const int64_t total = cum[E - 1];
+  const int64_t used = total < max_tiles ? total : max_tiles;
+  for (int64_t slot = tid; slot < max_tiles; slot += blockDim.x) {
+    int4 t = make_int4(-1, 0, 0, 0);
+    if (slot < used) {
+      // expert e: first with cum[e] > slot
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cum[mid] > slot) hi = mid; else lo = mid + 1;
+      }
+      const int e = lo;
+      const int64_t i = slot - (cum[e] - (n_s[e] + BM - 1) / BM);
+      const int64_t r0 = off_s[e] + i * BM;
+      int64_t rows = n_s[e] - i * BM < BM ? n_s[e] - i * BM : BM;
       if (r0 + rows > R) rows = R - r0 > 0 ? R - r0 : 0;  // memory safety against bad offsets
-      tiles[slot] = make_int4(rows > 0 ? tid : -1, static_cast<int>(r0), static_cast<int>(rows), 0);
+      t = make_int4(rows > 0 ? e : -1, static_cast<int>(r0), static_cast<int>(rows), 0);
     }
+    tiles[slot] = t;
   }
-  const int64_t used = start[E] < max_tiles ? start[E] : max_tiles;
-  for (int64_t i = used + tid; i < max_tiles; i += blockDim.x) tiles[i] = make_int4(-1, 0, 0, 0);
   if (tid == 0) tiles[max_tiles] = make_int4(static_cast<int>(used), 0, 0, 0);
 }
 

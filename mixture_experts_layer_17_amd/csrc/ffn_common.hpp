@@ -53,6 +53,37 @@ inline unsigned xcd_grid(int64_t total) {
   return static_cast<unsigned>(cdiv(total, kNumXcd) * kNumXcd);
 }
 
+// Weight-gradient tile order.  Expert e has a gm x gn grid of output tiles;
+// tiles in a block of GM x GN read the same GM operand slices along M and GN
+// along N.  Workgroups are handed to the XCDs round-robin by hardware id, so
+// the S = GM*GN tiles of one block get ids h, h+8, ..., h+8(S-1) (one XCD, one
+// L2), while the 8 blocks of a run of 8*S ids sit on 8 different XCDs (a heavily
+// loaded expert still spreads over the whole chip).  Returns false for ids
+// past the last tile; the grid is E*gm*gn.
+__device__ __forceinline__ bool wgrad_tile(int64_t h, int E, int gm, int gn, int& e, int& mt, int& nt) {
+  const int GM = gm % 2 == 0 ? 2 : 1;
+  const int GN = gn % 4 == 0 ? 4 : gn % 2 == 0 ? 2 : 1;
+  const int S = GM * GN;
+  const int64_t per_e = static_cast<int64_t>(gm / GM) * (gn / GN);
+  const int64_t ng = per_e * E;  // blocks
+  const int64_t run = h / (kNumXcd * S), q = h % (kNumXcd * S);
+  int64_t g;
+  int w;
+  if ((run + 1) * kNumXcd <= ng) {
+    g = run * kNumXcd + q % kNumXcd;
+    w = static_cast<int>(q / kNumXcd);
+  } else {  // last, partial run: blocks in hardware order
+    g = run * kNumXcd + q / S;
+    w = static_cast<int>(q % S);
+    if (g >= ng) return false;
+  }
+  e = static_cast<int>(g / per_e);
+  const int rem = static_cast<int>(g % per_e), bn = gn / GN;
+  mt = (rem / bn) * GM + w / GN;
+  nt = (rem % bn) * GN + w % GN;
+  return true;
+}
+
 // Launch the tile-table builder (defined in ffn.hip).
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
                      hipStream_t s);

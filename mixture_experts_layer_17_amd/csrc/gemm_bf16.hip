@@ -1,23 +1,40 @@
 // BF16 grouped expert-FFN GEMMs on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Two tile shapes share one kernel template: 256 x 256 outputs per workgroup
-// for large expert segments and the weight gradients, and 128 x 128 with 4
-// waves (each 64 x 64) for short segments (about 512 rows per expert), where a
-// 256-row tile would mostly compute padding.  The K loop steps by 64 through
-// two LDS stages with one or two register stages of global-load prefetch, one
-// barrier per step.  Every global load is a 16-byte vector and every operand keeps its
-// memory layout in LDS: K-contiguous operands (activation rows, the weights of
-// the dgrad GEMMs) are read as 16-byte fragments; operands contiguous along M
-// or N (the weights of the forward GEMMs, both operands of the weight-gradient
-// GEMMs, whose K is the token axis) are read with the gfx950 transposing LDS
-// read ds_read_b64_tr_b16, two per fragment.  Epilogues go through LDS so that
-// global stores (and the Hg/Hu loads of the SwiGLU backward) are 16-byte
-// vectors along rows.
+// Operand tiles move from global memory straight into LDS with the gfx950
+// 16-byte LDS-DMA buffer loads (buffer_load_dwordx4 ... lds): no register
+// staging, and an NS-stage LDS ring keeps NS-1 K-steps in flight while one is
+// consumed, with one barrier per K-step.  Buffer range checks supply the zeros
+// of ragged row tiles and of the token-axis tail of the weight gradients, so
+// the loads carry no predicates.
+//
+// Every operand keeps its memory layout in LDS, with 16-byte chunks XOR-
+// swizzled by row so that the fragment reads are free of bank conflicts:
+// K-contiguous operands (activation rows, the weights of the dgrad GEMMs) are
+// read as 16-byte fragments; operands contiguous along M or N (the weights of
+// the forward GEMMs, both operands of the weight-gradient GEMMs, whose K is the
+// token axis) are read with the transposing LDS read ds_read_b64_tr_b16, two
+// per fragment.  Two tile shapes: 256 x 256 outputs per workgroup (8 waves of
+// 128 x 64) for long expert segments and the weight gradients, 128 x 128 (4
+// waves of 64 x 64) for short segments.  Epilogues go through LDS so that
+// global stores (and the Hg/Hu loads of the SwiGLU backward) are 16-byte vectors.
 //
 // MFMA operand layout (32x32x16 bf16): lane l supplies A[m = l % 32][k = 8(l/32) .. +7]
 // and B[k = 8(l/32) .. +7][n = l % 32]; accumulator register r of lane l holds
 // C[8(r/4) + 4(l/32) + r%4][l % 32].
 #include "ffn_common.hpp"
+
+#ifndef MOE_BIG_BK
+#define MOE_BIG_BK 64
+#endif
+#ifndef MOE_BIG_NS
+#define MOE_BIG_NS 2
+#endif
+#ifndef MOE_SMALL_BK
+#define MOE_SMALL_BK 64
+#endif
+#ifndef MOE_SMALL_NS
+#define MOE_SMALL_NS 2
+#endif
 
 namespace moe {
 namespace {
@@ -25,130 +42,161 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kNoSplit = 0x7FFFFFFF;
-constexpr int kBK = 64;
-constexpr int kLdK = kBK + 8;  // K-contiguous LDS rows: 144 B, 16-byte reads of 16 rows cover all banks
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked, out of range reads 0
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Tile configuration: BM x BN outputs, WM x WN waves, DIST register stages of
-// global-load prefetch (1: tile kt+1 in flight, 2: tiles kt+1 and kt+2).
-template <int BM_, int BN_, int WM_, int WN_, int DIST_>
+// Tile configuration: BM x BN outputs, WM x WN waves, K-step BK, NS LDS stages.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, DIST = DIST_;
-  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  // M/N-contiguous LDS rows: rows + 32 elements.  A transposing read resolves
-  // banks over 32 lanes (four k-rows x 64 bytes); a row stride of 16 banks
-  // modulo 64 spreads them over all 64 banks.
-  static constexpr int ldm(int rows) { return rows + 32; }
-  static constexpr int tile(int rows) { return cmax(kBK * ldm(rows), rows * kLdK); }
-  static constexpr int kA = tile(BM), kB = tile(BN);
+  static constexpr int kA = BM * BK, kB = BN * BK;  // elements per stage
   static constexpr int kStage = kA + kB;
-  static constexpr int kLds = 2 * kStage;  // elements (bf16)
+  // epilogue tiles: G1 two BM x (BN/2 + 8), the others BM x (BN + 8) (G3 may halve)
+  static constexpr int kEpi = cmax(2 * BM * (BN / 2 + 8), BM * (BN + 8));
+  static constexpr int kLds = cmax(NS * kStage, kEpi);  // elements (bf16)
+  static_assert(BK == 32 || BK == 64, "K step");
 };
-#ifndef MOE_BIG_TILE
-#define MOE_BIG_TILE 1
+#ifndef MOE_BIG_WN
+#define MOE_BIG_WN 4
 #endif
-#if MOE_BIG_TILE == 1
-using Big = Cfg<256, 256, 2, 4, 1>;  // 8 waves of 128 x 64, one register stage
-#else
-using Big = Cfg<256, 256, 2, 2, 2>;  // 4 waves of 128 x 128, two register stages
-#endif
-using Small = Cfg<128, 128, 2, 2, 2>;
+using Big = Cfg<256, 256, 2, MOE_BIG_WN, MOE_BIG_BK, MOE_BIG_NS>;
+using Small = Cfg<128, 128, 2, 2, MOE_SMALL_BK, MOE_SMALL_NS>;
 
-// K-contiguous operand: element (mn, k) at p[mn*ld + k]; for k >= ksplit the
-// element comes from the second matrix at column k - ksplit.
+// K-contiguous operand: element (mn, k) at m0[mn*ld + k] for k < ksplit, else
+// m1[mn*ld + k - ksplit]; rows mn >= mn_valid read as zero.
 struct KcOp {
-  const uint16_t* p0;
-  const uint16_t* p1;
+  const uint16_t* m0;
+  const uint16_t* m1;
   int64_t ld;
   int ksplit;
   int mn_valid;
-  __device__ const uint16_t* at(int mn, int k) const {
-    return k < ksplit ? p0 + mn * ld + k : p1 + mn * ld + (k - ksplit);
-  }
 };
 
-// M/N-contiguous operand: element (mn, k) at p[k*ld + col].  With dual_w > 0 the
-// tile's N index alternates between two matrices in groups of dual_w/2 columns
-// (dual_w = one wave's N width), so every wave holds matching gate and up columns.
+// M/N-contiguous operand: element (mn, k) at m0[k*ld + c0 + mn]; k >= k_valid
+// reads as zero.  Dual: tile columns [0, W/2) come from m0 and [W/2, W) from
+// m1, both at column c0 + (mn mod W/2).
 struct McOp {
-  const uint16_t* p0;
-  const uint16_t* p1;
+  const uint16_t* m0;
+  const uint16_t* m1;
   int64_t ld;
-  int mn_valid;  // valid columns (of each matrix when dual)
+  int c0;
   int k_valid;
-  int dual_w;
-  __device__ void col_of(int mn, const uint16_t*& p, int& col) const {
-    if (dual_w > 0) {
-      const int h = dual_w / 2, w = mn / dual_w, r = mn % dual_w;
-      p = r >= h ? p1 : p0;
-      col = w * h + r % h;
-    } else {
-      p = p0;
-      col = mn;
-    }
-  }
 };
 
-// One operand's tile loader: 16-byte global loads into registers, 16-byte LDS
-// stores.  The M/N-contiguous form resolves each chunk's column pointer once
-// (the chunk keeps its M/N position for the whole K loop).
-template <class C, int ROWS, bool KC>
-struct Loader {
-  static constexpr int kChunks = ROWS * kBK / 8 / C::kThreads;
-  static_assert(kChunks >= 1 && ROWS * kBK / 8 % C::kThreads == 0, "tile does not split evenly");
-  static constexpr int kLd = C::ldm(ROWS);
-  uint4 v[kChunks];
+// Buffer descriptor over [base, base + bytes).  Every caller passes
+// workgroup-uniform values; readfirstlane keeps the descriptor in scalar
+// registers (a descriptor in vector registers would need a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int n = __builtin_amdgcn_readfirstlane(bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(bytes)));
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  void* pb = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pb, 0, n, kRsrcWord3);
+}
 
-  struct Bases {
-    const uint16_t* p[kChunks];
-  };
-  __device__ static void setup(const McOp& op, int tid, Bases& b) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int mn = ((tid + i * C::kThreads) % (ROWS / 8)) * 8;
-      const uint16_t* p;
-      int col;
-      op.col_of(mn, p, col);
-      b.p[i] = col < op.mn_valid ? p + col : nullptr;
-    }
-  }
-  __device__ static void setup(const KcOp&, int, Bases&) {}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_dst), 16, voff, 0, 0, 0);
+}
 
-  __device__ void load(const KcOp& op, const Bases&, int k0, int tid) {
+// 16-byte chunk swizzles.  K-contiguous tile rows hold BK elements; a fragment
+// read has 16 lanes on 16 consecutive rows at one chunk.  M/N-contiguous tile
+// rows (one k each) hold RS elements; a transposing read has 32 lanes on 4
+// consecutive k-rows x 4 consecutive chunks.
+template <int BK>
+__device__ __forceinline__ int kc_swz(int row) {
+  return BK == 64 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+template <int RS>
+__device__ __forceinline__ int mc_swz(int k) {
+  static_assert(RS >= 64, "M/N-contiguous tile rows of at least 64 elements");
+  return RS >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
+
+// Issue the LDS-DMA loads of a ROWS x BK K-contiguous tile (K-step at k0).
+template <class C, int ROWS>
+__device__ __forceinline__ void dma_kc(const KcOp& op, int k0, uint16_t* dst, int wave, int lane) {
+  constexpr int CPR = C::BK / 8;          // chunks per row
+  constexpr int RPI = 64 / CPR;           // rows per instruction (1 KB)
+  constexpr int NI = ROWS / RPI;
+  static_assert(NI % C::kWaves == 0, "K-contiguous tile does not split over the waves");
+  const bool hi = k0 >= op.ksplit;
+  const uint16_t* m = hi ? op.m1 : op.m0;
+  const int kk = hi ? k0 - op.ksplit : k0;
+  const int rows = op.mn_valid < ROWS ? op.mn_valid : ROWS;
+  const __amdgpu_buffer_rsrc_t r = rsrc(m, static_cast<int64_t>(rows) * op.ld * 2);
+  const int rl = lane / CPR, ph = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * C::kThreads;
-      const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      v[i] = row < op.mn_valid ? *reinterpret_cast<const uint4*>(op.at(row, k0 + kc)) : make_uint4(0, 0, 0, 0);
-    }
+  for (int u = 0; u < NI / C::kWaves; ++u) {
+    const int i = wave + u * C::kWaves;
+    const int row = i * RPI + rl;
+    const int lc = ph ^ kc_swz<C::BK>(row);
+    dma16(r, dst + i * 512, static_cast<int>((row * op.ld + kk + lc * 8) * 2));
   }
-  __device__ void load(const McOp& op, const Bases& b, int k0, int tid) {
+}
+
+// Issue the LDS-DMA loads of a BK x ROWS M/N-contiguous tile, as NSUB
+// sub-tiles of BK x ROWS/NSUB (dual: one per matrix).
+template <class C, int ROWS, int NSUB>
+__device__ __forceinline__ void dma_mc(const McOp& op, int k0, uint16_t* dst, int wave, int lane) {
+  constexpr int RS = ROWS / NSUB;
+  constexpr int CPR = RS / 8;             // chunks per k-row
+  constexpr int KPI = 64 / CPR;           // k-rows per instruction (1 KB)
+  constexpr int NIS = C::BK / KPI;        // instructions per sub-tile
+  constexpr int NI = NIS * NSUB;
+  static_assert(KPI >= 1 && C::BK % KPI == 0 && NI % C::kWaves == 0, "M/N-contiguous tile split");
+  int kv = op.k_valid - k0;
+  kv = kv < 0 ? 0 : (kv > C::BK ? C::BK : kv);
+  const int kl = lane / CPR, ph = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int k = k0 + (tid + i * C::kThreads) / (ROWS / 8);
-      v[i] = (b.p[i] != nullptr && k < op.k_valid) ? *reinterpret_cast<const uint4*>(b.p[i] + k * op.ld)
-                                                   : make_uint4(0, 0, 0, 0);
-    }
+  for (int u = 0; u < NI / C::kWaves; ++u) {
+    const int i = wave + u * C::kWaves;
+    const int sub = i / NIS, ii = i % NIS;
+    const uint16_t* m = (NSUB == 2 && sub == 1 ? op.m1 : op.m0) + k0 * op.ld;
+    const __amdgpu_buffer_rsrc_t r = rsrc(m, static_cast<int64_t>(kv) * op.ld * 2);
+    const int kr = ii * KPI + kl;
+    const int lc = ph ^ mc_swz<RS>(kr);
+    dma16(r, dst + sub * (C::BK * RS) + ii * 512, static_cast<int>((kr * op.ld + op.c0 + lc * 8) * 2));
   }
-  __device__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * C::kThreads;
-      if constexpr (KC) {
-        const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-        *reinterpret_cast<uint4*>(lds + row * kLdK + kc) = v[i];
-      } else {
-        const int kr = c / (ROWS / 8), mn = (c % (ROWS / 8)) * 8;
-        *reinterpret_cast<uint4*>(lds + kr * kLd + mn) = v[i];
-      }
-    }
-  }
-};
+}
+
+// MFMA fragment from a K-contiguous tile: rows base .. base+31, k-slice ks.
+template <class C>
+__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* t, int base, int ks, int lane) {
+  const int row = base + (lane & 31);
+  const int ph = (ks * 2 + (lane >> 5)) ^ kc_swz<C::BK>(row);
+  return *reinterpret_cast<const bf16x8*>(t + row * C::BK + ph * 8);
+}
+
+// MFMA fragment from an M/N-contiguous (sub-)tile of RS columns: columns
+// col .. col+31, k-slice ks.  Two transposing reads: within each 16-lane
+// group G, lane i gets slot s from element i%4 of the address of lane 4s + i/4;
+// lane L points at k-row 16 ks + 8(G/2) + 4 half + L/4, columns col + 16(G%2) + 4(L%4).
+template <class C, int RS>
+__device__ __forceinline__ bf16x8 frag_mc(const uint16_t* t, int col, int ks, int lane) {
+  const int G = lane >> 4, L = lane & 15;
+  const int k = ks * 16 + 8 * (G >> 1) + (L >> 2);
+  const int c = col + 16 * (G & 1) + 4 * (L & 3);
+  const int ph = (c >> 3) ^ mc_swz<RS>(k);  // same swizzle for k + 4
+  const uint16_t* p = t + k * RS + ph * 8 + (c & 7);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * RS));
+  bf16x8 r;
+  short tmp[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  __builtin_memcpy(&r, tmp, 16);
+  return r;
+}
+
+template <class C>
+using Acc = f32x16[C::TM][C::TN];
 
 template <bool KC>
 struct OpFor;
@@ -161,56 +209,91 @@ struct OpFor<false> {
   using T = McOp;
 };
 
-// MFMA fragment (8 consecutive k for one m or n) of the 32-row block starting at
-// `base` (M or N index) and k offset `k0` inside a stage.
-template <bool KC, int LDM>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* lds, int base, int k0, int lane) {
-  if constexpr (KC) {
-    return *reinterpret_cast<const bf16x8*>(lds + (base + (lane & 31)) * kLdK + k0 + (lane >> 5) * 8);
+template <class C, bool AKC, bool BKC, bool BDUAL>
+__device__ __forceinline__ bf16x8 frag_b(const uint16_t* Bs, int wn, int j, int ks, int lane) {
+  if constexpr (BKC) {
+    return frag_kc<C>(Bs, wn * C::WTN + j * 32, ks, lane);
+  } else if constexpr (BDUAL) {
+    // gate fragments j < TN/2, up fragments j >= TN/2, each matrix a BN/2-wide sub-tile
+    constexpr int H = C::TN / 2;
+    const int sub = j >= H ? 1 : 0;
+    return frag_mc<C, C::BN / 2>(Bs + sub * (C::BK * C::BN / 2), wn * (C::WTN / 2) + (j - sub * H) * 32, ks, lane);
   } else {
-    // Two transposing reads.  Within each 16-lane group G, lane i gets slot s
-    // from element i%4 of the address given by lane 4s + i/4; lane L points at
-    // row k = k0 + 8*(G/2) + 4*half + L/4, columns base + 16*(G%2) + 4*(L%4).
-    const int G = lane >> 4, L = lane & 15;
-    const uint16_t* p = lds + (k0 + 8 * (G >> 1) + (L >> 2)) * LDM + base + 16 * (G & 1) + 4 * (L & 3);
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * LDM));
-    bf16x8 r;
-    short tmp[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    __builtin_memcpy(&r, tmp, 16);
-    return r;
+    return frag_mc<C, C::BN>(Bs, wn * C::WTN + j * 32, ks, lane);
   }
 }
 
-template <class C>
-using Acc = f32x16[C::TM][C::TN];
+#ifndef MOE_FRAG_PIPE
+#define MOE_FRAG_PIPE 0
+#endif
+template <class C, bool AKC, bool BKC, bool BDUAL>
+__device__ __forceinline__ void load_frags(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int ks, int lane,
+                                           bf16x8* a, bf16x8* b) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+    a[i] = AKC ? frag_kc<C>(As, wm * C::WTM + i * 32, ks, lane) : frag_mc<C, C::BM>(As, wm * C::WTM + i * 32, ks, lane);
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) b[j] = frag_b<C, AKC, BKC, BDUAL>(Bs, wn, j, ks, lane);
+}
 
-template <class C, bool AKC, bool BKC>
+template <class C, bool AKC, bool BKC, bool BDUAL>
 __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs, int wm,
                                           int wn, int lane, Acc<C>& acc) {
+#if MOE_FRAG_PIPE
+  // fragments of k-slice ks+1 are read while the MFMAs of slice ks run
+  bf16x8 a[2][C::TM], b[2][C::TN];
+  load_frags<C, AKC, BKC, BDUAL>(As, Bs, wm, wn, 0, lane, a[0], b[0]);
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) {
+  for (int ks = 0; ks < C::BK / 16; ++ks) {
+    const int c = ks & 1;
+    if (ks + 1 < C::BK / 16) load_frags<C, AKC, BKC, BDUAL>(As, Bs, wm, wn, ks + 1, lane, a[c ^ 1], b[c ^ 1]);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+#if MOE_FRAG_PIPE == 2
+    if (ks + 1 < C::BK / 16) {
+      // one LDS read between consecutive MFMAs
+      constexpr int nr = C::TM * (AKC ? 1 : 2) + C::TN * (BKC ? 1 : 2);
+      constexpr int nm = C::TM * C::TN;
+#pragma unroll
+      for (int t = 0; t < (nr > nm ? nr : nm); ++t) {
+        if (t < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (t < nm) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+#endif
+  }
+#else
+#pragma unroll
+  for (int ks = 0; ks < C::BK / 16; ++ks) {
     bf16x8 a[C::TM], b[C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) a[i] = frag<AKC, C::ldm(C::BM)>(As, wm * C::WTM + i * 32, ks * 16, lane);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) b[j] = frag<BKC, C::ldm(C::BN)>(Bs, wn * C::WTN + j * 32, ks * 16, lane);
+    load_frags<C, AKC, BKC, BDUAL>(As, Bs, wm, wn, ks, lane, a, b);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
+#endif
 }
 
-// C = A B over K = [0, K).  Tile kt+2 is fetched into registers while tile kt
-// is consumed from LDS and tile kt+1 waits in the other register set, so every
-// global load has two compute steps to arrive.
-template <class C, bool AKC, bool BKC>
+// Wait until at most n LDS-DMA loads of this wave are outstanding (n < 16;
+// expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// C = A B over K = [0, K).  Stage kt lives in LDS slot kt % NS; the loads of
+// stage kt + NS - 1 are issued right after the barrier that retires stage kt - 1.
+template <class C, bool AKC, bool BKC, bool BDUAL>
 __device__ __forceinline__ void mainloop(const typename OpFor<AKC>::T& aop, const typename OpFor<BKC>::T& bop, int K,
                                          uint16_t* lds, int tid, Acc<C>& acc) {
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -218,69 +301,41 @@ __device__ __forceinline__ void mainloop(const typename OpFor<AKC>::T& aop, cons
     for (int j = 0; j < C::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nk = (K + kBK - 1) / kBK;
+  const int nk = (K + C::BK - 1) / C::BK;
   if (nk == 0) return;
-  using LA = Loader<C, C::BM, AKC>;
-  using LB = Loader<C, C::BN, BKC>;
-  typename LA::Bases ba;
-  typename LB::Bases bb;
-  LA::setup(aop, tid, ba);
-  LB::setup(bop, tid, bb);
-  if constexpr (C::DIST == 1) {
-    // one register stage: tile kt+1 is fetched while tile kt is consumed
-    LA la;
-    LB lb;
-    la.load(aop, ba, 0, tid);
-    lb.load(bop, bb, 0, tid);
-    la.store(lds, tid);
-    lb.store(lds + C::kA, tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      uint16_t* cur = lds + (kt & 1) * C::kStage;
-      uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStage;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        la.load(aop, ba, (kt + 1) * kBK, tid);
-        lb.load(bop, bb, (kt + 1) * kBK, tid);
-      }
-      mma_stage<C, AKC, BKC>(cur, cur + C::kA, wm, wn, lane, acc);
-      if (more) {
-        la.store(nxt, tid);
-        lb.store(nxt + C::kA, tid);
-      }
-      __syncthreads();
-    }
-    return;
-  }
-  LA la0, la1;
-  LB lb0, lb1;
-  la0.load(aop, ba, 0, tid);
-  lb0.load(bop, bb, 0, tid);
-  if (nk > 1) {
-    la1.load(aop, ba, kBK, tid);
-    lb1.load(bop, bb, kBK, tid);
-  }
-  la0.store(lds, tid);
-  lb0.store(lds + C::kA, tid);
-  __syncthreads();
-  auto step = [&](int kt, LA& la_next, LB& lb_next, LA& la_free, LB& lb_free) {
-    uint16_t* cur = lds + (kt & 1) * C::kStage;
-    uint16_t* nxt = lds + ((kt + 1) & 1) * C::kStage;
-    if (kt + 2 < nk) {
-      la_free.load(aop, ba, (kt + 2) * kBK, tid);
-      lb_free.load(bop, bb, (kt + 2) * kBK, tid);
-    }
-    mma_stage<C, AKC, BKC>(cur, cur + C::kA, wm, wn, lane, acc);
-    if (kt + 1 < nk) {
-      la_next.store(nxt, tid);
-      lb_next.store(nxt + C::kA, tid);
-    }
-    __syncthreads();
+  // LDS-DMA instructions per wave per stage
+  constexpr int kLA = (C::BM * C::BK * 2 / 1024) / C::kWaves;
+  constexpr int kLB = (C::BN * C::BK * 2 / 1024) / C::kWaves;
+  constexpr int kL = kLA + kLB;
+  static_assert(kL * (C::NS - 2) < 16, "too many loads in flight for the vmcnt immediate");
+  auto issue = [&](int kt) {
+    uint16_t* st = lds + (kt % C::NS) * C::kStage;
+    if constexpr (AKC) dma_kc<C, C::BM>(aop, kt * C::BK, st, wave, lane);
+    else dma_mc<C, C::BM, 1>(aop, kt * C::BK, st, wave, lane);
+    if constexpr (BKC) dma_kc<C, C::BN>(bop, kt * C::BK, st + C::kA, wave, lane);
+    else dma_mc<C, C::BN, BDUAL ? 2 : 1>(bop, kt * C::BK, st + C::kA, wave, lane);
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, la1, lb1, la0, lb0);
-    if (kt + 1 < nk) step(kt + 1, la0, lb0, la1, lb1);
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s)
+    if (s < nk) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = nk - 1 - kt < C::NS - 2 ? nk - 1 - kt : C::NS - 2;
+    if constexpr (C::NS >= 4) {
+      if (ahead >= 2) wait_vm<2 * kL>();
+      else if (ahead == 1) wait_vm<kL>();
+      else wait_vm<0>();
+    } else if constexpr (C::NS == 3) {
+      if (ahead >= 1) wait_vm<kL>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();
+    if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1);
+    const uint16_t* st = lds + (kt % C::NS) * C::kStage;
+    mma_stage<C, AKC, BKC, BDUAL>(st, st + C::kA, wm, wn, lane, acc);
   }
+  __syncthreads();  // the epilogue reuses the LDS
 }
 
 // ---------------------------------------------------------------------------
@@ -362,14 +417,16 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
     if (lid < 0) return;
     const int4 t = p.tiles[lid / gx];
     if (t.x < 0) return;
-    const int e = t.x, rows = t.z;
-    const int64_t row0 = t.y;
+    // tile-table values are workgroup-uniform: keep them (and the buffer
+    // descriptors built from them) in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(t.x), rows = __builtin_amdgcn_readfirstlane(t.z);
+    const int64_t row0 = __builtin_amdgcn_readfirstlane(t.y);
     const int nt = static_cast<int>(lid % gx);
     if constexpr (KIND == kG1) {
       const int n0 = nt * (C::BN / 2);
       const KcOp a{X + row0 * d, nullptr, d, kNoSplit, rows};
-      const McOp b{Wg + e * wsz + n0, Wu + e * wsz + n0, f, f - n0, d, C::WTN};
-      mainloop<C, true, false>(a, b, d, lds, tid, acc);
+      const McOp b{Wg + e * wsz, Wu + e * wsz, f, n0, d};
+      mainloop<C, true, false, true>(a, b, d, lds, tid, acc);
       // Hg and Hu tiles (BM x BN/2 each), then A in the Hg buffer
       constexpr int ldh = C::BN / 2 + 8;
       static_assert(2 * C::BM * ldh <= C::kLds, "G1 epilogue tiles exceed LDS");
@@ -405,14 +462,14 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
     } else if constexpr (KIND == kG2) {
       const int n0 = nt * C::BN;
       const KcOp a{static_cast<const uint16_t*>(p.act) + row0 * f, nullptr, f, kNoSplit, rows};
-      const McOp b{Wd + e * wsz + n0, nullptr, d, d - n0, f, 0};
-      mainloop<C, true, false>(a, b, f, lds, tid, acc);
+      const McOp b{Wd + e * wsz, nullptr, d, n0, f};
+      mainloop<C, true, false, false>(a, b, f, lds, tid, acc);
       store_acc<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
       const int n0 = nt * C::BN;  // over f
       const KcOp a{static_cast<const uint16_t*>(p.dy) + row0 * d, nullptr, d, kNoSplit, rows};
       const KcOp b{Wd + e * wsz + static_cast<int64_t>(n0) * d, nullptr, d, kNoSplit, f - n0};
-      mainloop<C, true, true>(a, b, d, lds, tid, acc);
+      mainloop<C, true, true, false>(a, b, d, lds, tid, acc);
       // SwiGLU backward: stage Hg, Hu with 16-byte loads, compute dHg, dHu in
       // place, 16-byte stores.  When both full tiles do not fit in LDS the tile
       // is processed in two row halves, each by the waves owning those rows.
@@ -455,28 +512,26 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
                    f, rows};
       const KcOp b{Wg + e * wsz + static_cast<int64_t>(n0) * f, Wu + e * wsz + static_cast<int64_t>(n0) * f, f, f,
                    d - n0};
-      mainloop<C, true, true>(a, b, 2 * f, lds, tid, acc);
+      mainloop<C, true, true, false>(a, b, 2 * f, lds, tid, acc);
       store_acc<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
     }
   } else {  // weight gradients: K = rows of expert e
-    // logical tile = (expert, M tile, N tile), N fastest, in hardware order so
-    // that a heavily loaded expert spreads over every XCD
+    // logical tile = (expert, M tile, N tile), blocks of tiles sharing operand
+    // slices kept on one XCD, an expert's blocks spread over all XCDs
     const int gm = KIND == kG4 ? (f + C::BM - 1) / C::BM : (d + C::BM - 1) / C::BM;
     const int gn = KIND == kG4 ? (d + C::BN - 1) / C::BN : 2 * ((f + C::BN - 1) / C::BN);
-    const int64_t lid = blockIdx.x;
-    if (lid >= static_cast<int64_t>(p.E) * gm * gn) return;
-    const int e = static_cast<int>(lid / (gm * gn));
-    const int mt = static_cast<int>((lid / gn) % gm), ntile = static_cast<int>(lid % gn);
-    const int64_t seg0 = p.offsets[e];
-    const int K = p.offsets[e + 1] - static_cast<int>(seg0);
+    int e, mt, ntile;
+    if (!wgrad_tile(blockIdx.x, p.E, gm, gn, e, mt, ntile)) return;
+    const int64_t seg0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+    const int K = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]) - static_cast<int>(seg0);
     const int m0 = mt * C::BM;
     uint16_t* Cp;
     int n0, ldc, mvalid, nvalid;
     McOp a, b;
     if constexpr (KIND == kG4) {  // dWd_e [f, d] = A_e^T dY_e
       n0 = ntile * C::BN;
-      a = McOp{static_cast<const uint16_t*>(p.act) + seg0 * f + m0, nullptr, f, f - m0, K, 0};
-      b = McOp{static_cast<const uint16_t*>(p.dy) + seg0 * d + n0, nullptr, d, d - n0, K, 0};
+      a = McOp{static_cast<const uint16_t*>(p.act) + seg0 * f, nullptr, f, m0, K};
+      b = McOp{static_cast<const uint16_t*>(p.dy) + seg0 * d, nullptr, d, n0, K};
       Cp = static_cast<uint16_t*>(p.o_dwd) + e * wsz;
       ldc = d;
       mvalid = f;
@@ -485,14 +540,14 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
       const int per = (f + C::BN - 1) / C::BN;
       const int which = ntile / per;
       n0 = (ntile % per) * C::BN;
-      a = McOp{X + seg0 * d + m0, nullptr, d, d - m0, K, 0};
-      b = McOp{static_cast<const uint16_t*>(which ? p.dhu : p.dhg) + seg0 * f + n0, nullptr, f, f - n0, K, 0};
+      a = McOp{X + seg0 * d, nullptr, d, m0, K};
+      b = McOp{static_cast<const uint16_t*>(which ? p.dhu : p.dhg) + seg0 * f, nullptr, f, n0, K};
       Cp = static_cast<uint16_t*>(which ? p.o_dwu : p.o_dwg) + e * wsz;
       ldc = f;
       mvalid = d;
       nvalid = f;
     }
-    mainloop<C, false, false>(a, b, K, lds, tid, acc);
+    mainloop<C, false, false, false>(a, b, K, lds, tid, acc);
     store_acc<C>(acc, lds, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0, tid);
   }
 }

@@ -1,47 +1,69 @@
 // Router logits l = x W_r and their backward (the linear router; the pages give
 // no router formula).  Small next to the expert GEMMs: the router is a [d, E]
-// matrix with E <= 256, so these are plain fp32-FMA kernels.
+// matrix with E <= 256, so these are plain fp32-FMA kernels bound by reading x.
 //
 // For E <= 16 (the linear-router workloads) W_r is staged in LDS and one wave
-// owns one token: 16-byte activation loads, per-lane expert sums reduced across
-// the wave (forward) or per-feature dot products over the experts (dx).  Wider
-// routers use plain one-thread-per-output kernels.  dW_r = x^T dl is reduced in
-// two deterministic passes: fixed 64-token chunks write fp32 partials to the
-// workspace, then one thread per (feature, expert) sums them in chunk order.
+// owns a token (two at a time, so that more loads are in flight): 16-byte
+// activation loads, per-lane expert sums reduced across the wave (forward) or
+// per-feature dot products over the experts (dx).  Wider routers use plain
+// one-thread-per-output kernels.  dW_r = x^T dl is reduced in two
+// deterministic passes: fixed token chunks write fp32 partials to the
+// workspace, then the partials are summed in chunk order.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kChunk = 32;        // tokens per dW_r partial
-constexpr int kTokPerBlk = 32;    // tokens per workgroup in the wave-per-token kernels
+constexpr int kChunk = 32;        // tokens per dW_r partial (generic path)
+constexpr int kDwTok = 64;        // tokens per dW_r partial (E <= 16 path)
+constexpr int kDwFeat = 512;      // features per workgroup of the E <= 16 dW_r path (64 lanes x 8)
+constexpr int kTokPerBlk = 16;    // tokens per workgroup in the wave-per-token kernels (4 per wave)
+constexpr int kTokPar = 2;        // tokens a wave works on at once
 constexpr size_t kMaxLdsW = 64 * 1024;
 
-// Row i of W_r [d, E] widened to fp32 from LDS (EP >= E experts, zero padded),
-// read as 16-byte vectors (EP * sizeof(T) is a multiple of 16).
+// W_r [d, E] in LDS, widened per read.  Feature i = V*c + q (c: 16-byte vector
+// of x, q: position in it) is stored at row q*nvec + c, so the lanes of a wave
+// (consecutive c) read consecutive rows; rows hold EP >= E experts, zero padded.
 template <typename T, int EP>
-__device__ __forceinline__ void w_row(const T* __restrict__ wl, int i, float* o) {
+__device__ __forceinline__ void w_row(const T* __restrict__ wl, int nvec, int c, int q, float* o) {
   constexpr int V = Elem<T>::kVec;
   static_assert(EP % V == 0, "W_r rows must be whole 16-byte vectors");
-  const uint4* r = reinterpret_cast<const uint4*>(wl + static_cast<int64_t>(i) * EP);
+  const uint4* r = reinterpret_cast<const uint4*>(wl + (static_cast<int64_t>(q) * nvec + c) * EP);
 #pragma unroll
-  for (int q = 0; q < EP / V; ++q) Elem<T>::unpack(r[q], o + q * V);
+  for (int u = 0; u < EP / V; ++u) Elem<T>::unpack(r[u], o + u * V);
 }
 
 template <typename T, int EP>
 __device__ __forceinline__ void stage_w(const T* __restrict__ w, int d, int E, T* wl) {
+  constexpr int V = Elem<T>::kVec;
+  const int nvec = d / V;
+  if (E == EP) {
+    // rows of W_r are whole 16-byte vectors: one vector load per (row, part)
+    constexpr int P = EP / V;  // vectors per row
+    const uint4* src = reinterpret_cast<const uint4*>(w);
+#pragma unroll 8
+    for (int i = threadIdx.x; i < d * P; i += blockDim.x) {
+      const int r = i / P, u = i - r * P;
+      const int c = r / V, q = r - c * V;
+      reinterpret_cast<uint4*>(wl + (static_cast<int64_t>(q) * nvec + c) * EP)[u] = src[i];
+    }
+    __syncthreads();
+    return;
+  }
   for (int i = threadIdx.x; i < d * EP; i += blockDim.x) {
     const int r = i / EP, e = i - r * EP;
+    const int c = r / V, q = r - c * V;
+    const int64_t o = (static_cast<int64_t>(q) * nvec + c) * EP + e;
     if constexpr (sizeof(T) == 4)
-      wl[i] = e < E ? w[static_cast<int64_t>(r) * E + e] : 0.f;
+      wl[o] = e < E ? w[static_cast<int64_t>(r) * E + e] : 0.f;
     else
-      wl[i] = e < E ? w[static_cast<int64_t>(r) * E + e] : static_cast<T>(0);
+      wl[o] = e < E ? w[static_cast<int64_t>(r) * E + e] : static_cast<T>(0);
   }
   __syncthreads();
 }
 
-// logits: one wave per token, 16-byte activation loads, per-lane expert sums
-// reduced across the wave.  W_r is staged in LDS once per workgroup.
+// logits: a wave takes kTokPar tokens at a time, 16-byte activation loads,
+// per-lane expert sums reduced across the wave.  W_r is staged once per workgroup.
 template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_fwd_fast_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                              int64_t Tn, int d, int E, float* __restrict__ logits) {
@@ -49,35 +71,53 @@ __global__ __launch_bounds__(256) void router_fwd_fast_kernel(const T* __restric
   T* wl = reinterpret_cast<T*>(smem_raw);
   stage_w<T, EP>(w, d, E, wl);
   constexpr int V = Elem<T>::kVec;
+  constexpr int kPerWave = kTokPerBlk / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvec = d / V;
-  for (int tl = wave; tl < kTokPerBlk; tl += 4) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + tl;
-    if (t >= Tn) break;
-    float acc[EP];
+  const int64_t tw = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + wave * kPerWave;
+  for (int tt = 0; tt < kPerWave; tt += kTokPar) {
+    float acc[kTokPar][EP];
 #pragma unroll
-    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * d);
+    for (int p = 0; p < kTokPar; ++p)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) acc[p][e] = 0.f;
     for (int c = lane; c < nvec; c += 64) {
-      float xv[V];
-      Elem<T>::unpack(xr[c], xv);
+      float xv[kTokPar][V];
+#pragma unroll
+      for (int p = 0; p < kTokPar; ++p) {
+        const int64_t t = tw + tt + p;
+        if (t < Tn) {
+          Elem<T>::unpack(reinterpret_cast<const uint4*>(x + t * d)[c], xv[p]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < V; ++q) xv[p][q] = 0.f;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < V; ++q) {
         float wr[EP];
-        w_row<T, EP>(wl, c * V + q, wr);
+        w_row<T, EP>(wl, nvec, c, q, wr);
 #pragma unroll
-        for (int e = 0; e < EP; ++e) acc[e] += xv[q] * wr[e];
+        for (int p = 0; p < kTokPar; ++p)
+#pragma unroll
+          for (int e = 0; e < EP; ++e) acc[p][e] += xv[p][q] * wr[e];
       }
     }
 #pragma unroll
-    for (int e = 0; e < EP; ++e) acc[e] = wave_sum(acc[e]);
+    for (int p = 0; p < kTokPar; ++p) {
+      const int64_t t = tw + tt + p;
 #pragma unroll
-    for (int e = 0; e < EP; ++e)
-      if (lane == e && e < E) logits[t * E + e] = acc[e];
+      for (int e = 0; e < EP; ++e) acc[p][e] = wave_sum(acc[p][e]);
+      if (t < Tn) {
+#pragma unroll
+        for (int e = 0; e < EP; ++e)
+          if (lane == e && e < E) logits[t * E + e] = acc[p][e];
+      }
+    }
   }
 }
 
-// dx (+)= dl W_r^T: one wave per token, 16-byte output vectors.
+// dx (+)= dl W_r^T: a wave takes kTokPar tokens at a time, 16-byte output vectors.
 template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_bwd_dx_fast_kernel(const float* __restrict__ dl,
                                                                 const T* __restrict__ w, int64_t Tn, int d, int E,
@@ -86,78 +126,132 @@ __global__ __launch_bounds__(256) void router_bwd_dx_fast_kernel(const float* __
   T* wl = reinterpret_cast<T*>(smem_raw);
   stage_w<T, EP>(w, d, E, wl);
   constexpr int V = Elem<T>::kVec;
+  constexpr int kPerWave = kTokPerBlk / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvec = d / V;
-  for (int tl = wave; tl < kTokPerBlk; tl += 4) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + tl;
-    if (t >= Tn) break;
-    float g[EP];
+  const int64_t tw = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + wave * kPerWave;
+  for (int tt = 0; tt < kPerWave; tt += kTokPar) {
+    float g[kTokPar][EP];
 #pragma unroll
-    for (int e = 0; e < EP; ++e) g[e] = e < E ? dl[t * E + e] : 0.f;
-    uint4* out = reinterpret_cast<uint4*>(dx + t * d);
+    for (int p = 0; p < kTokPar; ++p) {
+      const int64_t t = tw + tt + p;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) g[p][e] = (t < Tn && e < E) ? dl[t * E + e] : 0.f;
+    }
     for (int c = lane; c < nvec; c += 64) {
-      float o[V];
-      if (accumulate) {
-        Elem<T>::unpack(out[c], o);
-      } else {
+      float o[kTokPar][V];
 #pragma unroll
-        for (int q = 0; q < V; ++q) o[q] = 0.f;
+      for (int p = 0; p < kTokPar; ++p) {
+        const int64_t t = tw + tt + p;
+        if (accumulate && t < Tn) {
+          Elem<T>::unpack(reinterpret_cast<const uint4*>(dx + t * d)[c], o[p]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < V; ++q) o[p][q] = 0.f;
+        }
       }
 #pragma unroll
       for (int q = 0; q < V; ++q) {
         float wr[EP];
-        w_row<T, EP>(wl, c * V + q, wr);
-        float s = 0.f;
+        w_row<T, EP>(wl, nvec, c, q, wr);
 #pragma unroll
-        for (int e = 0; e < EP; ++e) s += g[e] * wr[e];
-        o[q] += s;
+        for (int p = 0; p < kTokPar; ++p) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EP; ++e) s += g[p][e] * wr[e];
+          o[p][q] += s;
+        }
       }
-      out[c] = Elem<T>::pack(o);
+#pragma unroll
+      for (int p = 0; p < kTokPar; ++p) {
+        const int64_t t = tw + tt + p;
+        if (t < Tn) reinterpret_cast<uint4*>(dx + t * d)[c] = Elem<T>::pack(o[p]);
+      }
     }
   }
 }
 
-// dW_r partials over fixed 64-token chunks: thread = 8 consecutive features x
-// all experts; the chunk's dl rows are staged in LDS.
+// dW_r partials, E <= 16: workgroup = (64-token chunk, 512 features); wave w
+// takes tokens w, w+4, ... of the chunk, lane = 8 consecutive features x EP
+// experts.  The four waves' sums are added in wave order through LDS and
+// written as part[chunk][feature group][q][lane][EP] (feature = group*512 +
+// 8*lane + q), so every store of a wave is one contiguous run.
 template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_bwd_dw_fast_kernel(const T* __restrict__ x,
                                                                 const float* __restrict__ dl, int64_t Tn, int d,
                                                                 int E, float* __restrict__ part) {
-  __shared__ float dls[kChunk * EP];
+  __shared__ float dls[kDwTok * EP];
+  __shared__ float red[4][64][EP + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
-  const int64_t t0 = c * kChunk;
-  const int nt = static_cast<int>(Tn - t0 < kChunk ? Tn - t0 : kChunk);
-  for (int i = threadIdx.x; i < kChunk * EP; i += blockDim.x) {
+  const int fg = blockIdx.y, ng = gridDim.y;
+  const int64_t t0 = c * kDwTok;
+  const int nt = static_cast<int>(Tn - t0 < kDwTok ? Tn - t0 : kDwTok);
+  for (int i = tid; i < kDwTok * EP; i += blockDim.x) {
     const int r = i / EP, e = i - r * EP;
     dls[i] = (r < nt && e < E) ? dl[(t0 + r) * E + e] : 0.f;
   }
   __syncthreads();
-  const int i0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
-  if (i0 >= d) return;
+  const int i0 = fg * kDwFeat + lane * 8;
   float acc[8][EP];
 #pragma unroll
   for (int q = 0; q < 8; ++q)
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[q][e] = 0.f;
-  for (int r = 0; r < nt; ++r) {
-    float xv[8];
-    if constexpr (sizeof(T) == 2) {
-      Elem<T>::unpack(*reinterpret_cast<const uint4*>(x + (t0 + r) * d + i0), xv);
-    } else {
-      Elem<T>::unpack(reinterpret_cast<const uint4*>(x + (t0 + r) * d + i0)[0], xv);
-      Elem<T>::unpack(reinterpret_cast<const uint4*>(x + (t0 + r) * d + i0)[1], xv + 4);
+  if (i0 < d) {
+    for (int r = wave; r < nt; r += 4) {
+      float xv[8];
+      const T* xr = x + (t0 + r) * d + i0;
+      if constexpr (sizeof(T) == 2) {
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(xr), xv);
+      } else {
+        Elem<T>::unpack(reinterpret_cast<const uint4*>(xr)[0], xv);
+        Elem<T>::unpack(reinterpret_cast<const uint4*>(xr)[1], xv + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < EP; ++e) acc[q][e] += xv[q] * dls[r * EP + e];
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int e = 0; e < EP; ++e) acc[q][e] += xv[q] * dls[r * EP + e];
   }
-  const int64_t n = static_cast<int64_t>(d) * E;
+  float* out = part + (c * ng + fg) * static_cast<int64_t>(kDwFeat * EP);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
+  for (int q = 0; q < 8; ++q) {
 #pragma unroll
-    for (int e = 0; e < EP; ++e)
-      if (e < E) part[c * n + static_cast<int64_t>(i0 + q) * E + e] = acc[q][e];
+    for (int e = 0; e < EP; ++e) red[wave][lane][e] = acc[q][e];
+    __syncthreads();
+    for (int o = tid; o < 64 * EP; o += blockDim.x) {
+      const int l = o / EP, e = o - l * EP;
+      out[q * 64 * EP + o] = ((red[0][l][e] + red[1][l][e]) + red[2][l][e]) + red[3][l][e];
+    }
+    __syncthreads();
+  }
+}
+
+// Sum of the E <= 16 partials in chunk order; thread j follows the partial layout.
+template <typename T, int EP>
+__global__ __launch_bounds__(256) void router_bwd_dw_fast_reduce_kernel(const float* __restrict__ part, int nchunk,
+                                                                       int ng, int d, int E, T* __restrict__ dw) {
+  const int64_t per = static_cast<int64_t>(ng) * kDwFeat * EP;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= per) return;
+  const int e = static_cast<int>(j % EP);
+  const int l = static_cast<int>((j / EP) % 64);
+  const int q = static_cast<int>((j / (EP * 64)) % 8);
+  const int fg = static_cast<int>(j / (EP * kDwFeat));
+  const int i = fg * kDwFeat + l * 8 + q;
+  if (e >= E || i >= d) return;
+  float acc = 0.f;
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(c + u) * per + j];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; c < nchunk; ++c) acc += part[c * per + j];
+  Elem<T>::store1(dw, static_cast<int64_t>(i) * E + e, acc);
 }
 
 template <typename T>
@@ -264,35 +358,45 @@ int router_fwd_impl(const void* x, const void* w_r, int64_t Tn, int d, int E, fl
   return launch_status();
 }
 
+template <typename T, int EP>
+void router_bwd_fast(const void* x, const void* w_r, const float* dlogits, int64_t Tn, int d, int E, void* dx,
+                     int accumulate_dx, void* dw_r, float* part, hipStream_t s) {
+  const dim3 g(static_cast<unsigned>(cdiv(Tn, kTokPerBlk)));
+  MOE_LAUNCH("router_bwd_dx", (router_bwd_dx_fast_kernel<T, EP>), g, dim3(256),
+             static_cast<size_t>(d) * EP * sizeof(T), s, dlogits, static_cast<const T*>(w_r), Tn, d, E,
+             static_cast<T*>(dx), accumulate_dx);
+  const int nchunk = static_cast<int>(cdiv(Tn, kDwTok));
+  const int ng = static_cast<int>(cdiv(d, kDwFeat));
+  MOE_LAUNCH("router_bwd_dw_partial", (router_bwd_dw_fast_kernel<T, EP>),
+             dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(ng)), dim3(256), 0, s,
+             static_cast<const T*>(x), dlogits, Tn, d, E, part);
+  const int64_t per = static_cast<int64_t>(ng) * kDwFeat * EP;
+  MOE_LAUNCH("router_bwd_dw_reduce", (router_bwd_dw_fast_reduce_kernel<T, EP>),
+             dim3(static_cast<unsigned>(cdiv(per, 256))), dim3(256), 0, s, part, nchunk, ng, d, E,
+             static_cast<T*>(dw_r));
+}
+
 template <typename T>
 int router_bwd_impl(const void* x, const void* w_r, const float* dlogits, int64_t Tn, int d, int E, void* dx,
                     int accumulate_dx, void* dw_r, float* part, hipStream_t s) {
-  const dim3 g(static_cast<unsigned>(cdiv(Tn, kTokPerBlk)));
+  if (fast_ok<T, 8>(d, E)) {
+    router_bwd_fast<T, 8>(x, w_r, dlogits, Tn, d, E, dx, accumulate_dx, dw_r, part, s);
+    return launch_status();
+  }
+  if (fast_ok<T, 16>(d, E)) {
+    router_bwd_fast<T, 16>(x, w_r, dlogits, Tn, d, E, dx, accumulate_dx, dw_r, part, s);
+    return launch_status();
+  }
   const int64_t n = static_cast<int64_t>(d) * E;
   const int nchunk = static_cast<int>(cdiv(Tn, kChunk));
-  const dim3 gdw(static_cast<unsigned>(nchunk), static_cast<unsigned>(cdiv(d / 8, 256)));
-  if (fast_ok<T, 8>(d, E)) {
-    MOE_LAUNCH("router_bwd_dx", (router_bwd_dx_fast_kernel<T, 8>), g, dim3(256),
-               static_cast<size_t>(d) * 8 * sizeof(T), s, dlogits, static_cast<const T*>(w_r), Tn, d, E,
-               static_cast<T*>(dx), accumulate_dx);
-    MOE_LAUNCH("router_bwd_dw_partial", (router_bwd_dw_fast_kernel<T, 8>), gdw, dim3(256), 0, s,
-               static_cast<const T*>(x), dlogits, Tn, d, E, part);
-  } else if (fast_ok<T, 16>(d, E)) {
-    MOE_LAUNCH("router_bwd_dx", (router_bwd_dx_fast_kernel<T, 16>), g, dim3(256),
-               static_cast<size_t>(d) * 16 * sizeof(T), s, dlogits, static_cast<const T*>(w_r), Tn, d, E,
-               static_cast<T*>(dx), accumulate_dx);
-    MOE_LAUNCH("router_bwd_dw_partial", (router_bwd_dw_fast_kernel<T, 16>), gdw, dim3(256), 0, s,
-               static_cast<const T*>(x), dlogits, Tn, d, E, part);
-  } else {
-    const int64_t nch = Tn * (d / 8);
-    MOE_LAUNCH("router_bwd_dx", router_bwd_dx_kernel<T>, dim3(static_cast<unsigned>(cdiv(nch, 256))), dim3(256), 0,
-               s, dlogits, static_cast<const T*>(w_r), Tn, d, E, static_cast<T*>(dx), accumulate_dx);
-    MOE_LAUNCH("router_bwd_dw_partial", router_bwd_dw_partial_kernel<T>,
-               dim3(static_cast<unsigned>(cdiv(n, 256)), nchunk), dim3(256), 0, s, static_cast<const T*>(x), dlogits,
-               Tn, d, E, part);
-  }
-  MOE_LAUNCH("router_bwd_dw_reduce", router_bwd_dw_reduce_kernel<T>, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s,
-                     part, nchunk, n, static_cast<T*>(dw_r));
+  const int64_t nch = Tn * (d / 8);
+  MOE_LAUNCH("router_bwd_dx", router_bwd_dx_kernel<T>, dim3(static_cast<unsigned>(cdiv(nch, 256))), dim3(256), 0, s,
+             dlogits, static_cast<const T*>(w_r), Tn, d, E, static_cast<T*>(dx), accumulate_dx);
+  MOE_LAUNCH("router_bwd_dw_partial", router_bwd_dw_partial_kernel<T>,
+             dim3(static_cast<unsigned>(cdiv(n, 256)), nchunk), dim3(256), 0, s, static_cast<const T*>(x), dlogits,
+             Tn, d, E, part);
+  MOE_LAUNCH("router_bwd_dw_reduce", router_bwd_dw_reduce_kernel<T>, dim3(static_cast<unsigned>(cdiv(n, 256))),
+             dim3(256), 0, s, part, nchunk, n, static_cast<T*>(dw_r));
   return launch_status();
 }
 
@@ -313,7 +417,11 @@ extern "C" int moe_router_logits(const void* x, const void* w_r, int dtype, int6
 
 extern "C" size_t moe_router_logits_bwd_workspace(int64_t T, int32_t d, int32_t E) {
   if (T < 0 || d <= 0 || E <= 0) return 0;
-  return static_cast<size_t>(cdiv(T, kChunk) > 0 ? cdiv(T, kChunk) : 1) * d * E * sizeof(float);
+  // generic path: [ceil(T/32)][d][E]; E <= 16 path: [ceil(T/64)][ceil(d/512)*512][EP]
+  const size_t generic = static_cast<size_t>(cdiv(T, kChunk) > 0 ? cdiv(T, kChunk) : 1) * d * E;
+  const int ep = E <= 8 ? 8 : 16;
+  const size_t fast = static_cast<size_t>(cdiv(T, kDwTok) > 0 ? cdiv(T, kDwTok) : 1) * cdiv(d, kDwFeat) * kDwFeat * ep;
+  return (generic > fast ? generic : fast) * sizeof(float);
 }
 
 extern "C" int moe_router_logits_bwd(const void* x, const void* w_r, int dtype, const float* dlogits, int64_t T,
