@@ -15,14 +15,51 @@ is the fp64 oracle timed on a bounded token sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 METRIC = "MoE layer fwd+bwd tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak), 1 GPU"
 PEAK = {"bf16": 2.5e15, "mxfp8": 5.0e15, "f32": 157.3e12}   # dense MFMA, FLOP/s
 HBM_PEAK = 8.0e12                                            # bytes/s
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_digest() -> str:
+    """sha256 prefix of the library's HIP sources and C header."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_17_amd", "csrc")
+    for f in sorted(x for x in os.listdir(csrc) if x.endswith((".hip", ".hpp"))):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "moe.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(tag: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
+    (already scaled by the copy calibration), or None when there is no summary for this workload or
+    the library sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{tag}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        txt = fh.read()
+    m = re.search(r"^source-digest: (\w+)", txt, re.M)
+    if not m or m.group(1) != source_digest():
+        return None
+    for line in txt.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and (cells[0] == kernel or cells[0].startswith(kernel + " ")):
+            return float(cells[6]) * 1e6
+    return None
 
 
 def kernel_work(name: str, w, s: int) -> tuple[str, float]:
@@ -145,15 +182,20 @@ def main() -> int:
     dom = max(per_step_us, key=per_step_us.get)
     bound, work = kernel_work(dom, w, s)
     avg_s = per_launch_us[dom] * 1e-6
+    tag = f"{w.name.replace('-', '_')}_T{w.T}"
+    traffic = counted_traffic(tag, dom)
     if bound == "mfma":
         peak = PEAK[w.prec]
         roof = {"bound": "mfma", "kernel": dom, "achieved": work / avg_s / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": work / avg_s / peak, "traffic": None,
+                "unit": "TFLOP/s", "frac": work / avg_s / peak, "traffic": traffic,
                 "work_per_launch": f"{work:.4g} FLOP", "avg_launch_us": per_launch_us[dom]}
     else:
         roof = {"bound": "hbm", "kernel": dom, "achieved": work / avg_s / 1e9, "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": work / avg_s / HBM_PEAK, "traffic": None,
+                "unit": "GB/s", "frac": work / avg_s / HBM_PEAK, "traffic": traffic,
                 "work_per_launch": f"{work:.4g} B", "avg_launch_us": per_launch_us[dom]}
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, copy-calibrated)"
+    roof["traffic_source"] = f"profiles/{tag}_hbm_traffic.md" if traffic is not None else \
+        "null: no counter summary taken with the current kernel sources"
     memk = {}
     for name in ("dispatch", "combine", "combine_bwd", "dispatch_bwd"):
         if name in per_launch_us:

@@ -2,7 +2,7 @@
 //
 // Operand tiles move from global memory straight into LDS with the gfx950
 // 16-byte LDS-DMA buffer loads (buffer_load_dwordx4 ... lds): no register
-// staging, and an NS-stage LDS ring keeps NS-1 K-steps in flight while one is
+// staging, and a 2- or 3-deep LDS ring per operand keeps K-steps in flight while one is
 // consumed, with one barrier per K-step.  Buffer range checks supply the zeros
 // of ragged row tiles and of the token-axis tail of the weight gradients, so
 // the loads carry no predicates.
@@ -26,14 +26,8 @@
 #ifndef MOE_BIG_BK
 #define MOE_BIG_BK 64
 #endif
-#ifndef MOE_BIG_NS
-#define MOE_BIG_NS 2
-#endif
 #ifndef MOE_SMALL_BK
 #define MOE_SMALL_BK 64
-#endif
-#ifndef MOE_SMALL_NS
-#define MOE_SMALL_NS 2
 #endif
 
 namespace moe {
@@ -49,25 +43,40 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format: range
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Tile configuration: BM x BN outputs, WM x WN waves, K-step BK, NS LDS stages.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
+// Tile configuration: BM x BN outputs, WM x WN waves, K-step BK, LDS ring of
+// NA stages for the A tile and NB stages for the B tile (2 or 3, not both 3).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NA_, int NB_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NA = NA_, NB = NB_;
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int kA = BM * BK, kB = BN * BK;  // elements per stage
-  static constexpr int kStage = kA + kB;
+  static constexpr int kBOff = NA * kA;              // the B ring follows the A ring
   // epilogue tiles: G1 two BM x (BN/2 + 8), the others BM x (BN + 8) (G3 may halve)
   static constexpr int kEpi = cmax(2 * BM * (BN / 2 + 8), BM * (BN + 8));
-  static constexpr int kLds = cmax(NS * kStage, kEpi);  // elements (bf16)
+  static constexpr int kLds = cmax(NA * kA + NB * kB, kEpi);  // elements (bf16)
   static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(NA >= 2 && NA <= 3 && NB >= 2 && NB <= 3 && NA + NB <= 5, "LDS ring depth");
+  static_assert(kLds * 2 <= 160 * 1024, "LDS budget");
 };
 #ifndef MOE_BIG_WN
 #define MOE_BIG_WN 4
 #endif
-using Big = Cfg<256, 256, 2, MOE_BIG_WN, MOE_BIG_BK, MOE_BIG_NS>;
-using Small = Cfg<128, 128, 2, 2, MOE_SMALL_BK, MOE_SMALL_NS>;
+#ifndef MOE_BIG_NA
+#define MOE_BIG_NA 2
+#endif
+#ifndef MOE_BIG_NB
+#define MOE_BIG_NB 2
+#endif
+#ifndef MOE_SMALL_NA
+#define MOE_SMALL_NA 3
+#endif
+#ifndef MOE_SMALL_NB
+#define MOE_SMALL_NB 2
+#endif
+using Big = Cfg<256, 256, 2, MOE_BIG_WN, MOE_BIG_BK, MOE_BIG_NA, MOE_BIG_NB>;
+using Small = Cfg<128, 128, 2, 2, MOE_SMALL_BK, MOE_SMALL_NA, MOE_SMALL_NB>;
 
 // K-contiguous operand: element (mn, k) at m0[mn*ld + k] for k < ksplit, else
 // m1[mn*ld + k - ksplit]; rows mn >= mn_valid read as zero.
@@ -279,16 +288,19 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const
 #endif
 }
 
-// Wait until at most n LDS-DMA loads of this wave are outstanding (n < 16;
-// expcnt and lgkmcnt left alone).
+// Wait until at most N LDS-DMA loads of this wave are outstanding (N < 16;
+// expcnt and lgkmcnt left alone).  Loads complete in issue order.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
 
-// C = A B over K = [0, K).  Stage kt lives in LDS slot kt % NS; the loads of
-// stage kt + NS - 1 are issued right after the barrier that retires stage kt - 1.
+// C = A B over K = [0, K).  K-step kt of A lives in A slot kt % NA and of B in
+// B slot kt % NB.  Right after the barrier that retires step kt - 1, step
+// kt + N - 1 of each operand is issued, the 2-deep operand first; so when step
+// kt + 1 is waited for, only the loads of the 3-deep operand's step kt + 2 (if
+// any) were issued after the last load it needs.
 template <class C, bool AKC, bool BKC, bool BDUAL>
 __device__ __forceinline__ void mainloop(const typename OpFor<AKC>::T& aop, const typename OpFor<BKC>::T& bop, int K,
                                          uint16_t* lds, int tid, Acc<C>& acc) {
@@ -303,37 +315,40 @@ __device__ __forceinline__ void mainloop(const typename OpFor<AKC>::T& aop, cons
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (K + C::BK - 1) / C::BK;
   if (nk == 0) return;
-  // LDS-DMA instructions per wave per stage
+  // LDS-DMA instructions per wave per K-step
   constexpr int kLA = (C::BM * C::BK * 2 / 1024) / C::kWaves;
   constexpr int kLB = (C::BN * C::BK * 2 / 1024) / C::kWaves;
-  constexpr int kL = kLA + kLB;
-  static_assert(kL * (C::NS - 2) < 16, "too many loads in flight for the vmcnt immediate");
-  auto issue = [&](int kt) {
-    uint16_t* st = lds + (kt % C::NS) * C::kStage;
+  constexpr int kAhead = C::NA == 3 ? kLA : (C::NB == 3 ? kLB : 0);
+  auto issue_a = [&](int kt) {
+    uint16_t* st = lds + (kt % C::NA) * C::kA;
     if constexpr (AKC) dma_kc<C, C::BM>(aop, kt * C::BK, st, wave, lane);
     else dma_mc<C, C::BM, 1>(aop, kt * C::BK, st, wave, lane);
-    if constexpr (BKC) dma_kc<C, C::BN>(bop, kt * C::BK, st + C::kA, wave, lane);
-    else dma_mc<C, C::BN, BDUAL ? 2 : 1>(bop, kt * C::BK, st + C::kA, wave, lane);
   };
-#pragma unroll
-  for (int s = 0; s < C::NS - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = nk - 1 - kt < C::NS - 2 ? nk - 1 - kt : C::NS - 2;
-    if constexpr (C::NS >= 4) {
-      if (ahead >= 2) wait_vm<2 * kL>();
-      else if (ahead == 1) wait_vm<kL>();
-      else wait_vm<0>();
-    } else if constexpr (C::NS == 3) {
-      if (ahead >= 1) wait_vm<kL>();
-      else wait_vm<0>();
+  auto issue_b = [&](int kt) {
+    uint16_t* st = lds + C::kBOff + (kt % C::NB) * C::kB;
+    if constexpr (BKC) dma_kc<C, C::BN>(bop, kt * C::BK, st, wave, lane);
+    else dma_mc<C, C::BN, BDUAL ? 2 : 1>(bop, kt * C::BK, st, wave, lane);
+  };
+  auto issue = [&](int ka, int kb) {  // 2-deep operand first
+    if constexpr (C::NA == 3) {
+      if (kb < nk) issue_b(kb);
+      if (ka < nk) issue_a(ka);
     } else {
-      wait_vm<0>();
+      if (ka < nk) issue_a(ka);
+      if (kb < nk) issue_b(kb);
     }
+  };
+  issue(0, 0);
+  if (C::NA == 3) issue(1, nk);
+  if (C::NB == 3) issue(nk, 1);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) wait_vm<kAhead>();
+    else wait_vm<0>();
     __syncthreads();
-    if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1);
-    const uint16_t* st = lds + (kt % C::NS) * C::kStage;
-    mma_stage<C, AKC, BKC, BDUAL>(st, st + C::kA, wm, wn, lane, acc);
+    issue(kt + C::NA - 1, kt + C::NB - 1);
+    const uint16_t* as = lds + (kt % C::NA) * C::kA;
+    const uint16_t* bs = lds + C::kBOff + (kt % C::NB) * C::kB;
+    mma_stage<C, AKC, BKC, BDUAL>(as, bs, wm, wn, lane, acc);
   }
   __syncthreads();  // the epilogue reuses the LDS
 }
