@@ -188,7 +188,8 @@ int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, co
  *           each segment and a segment's last block is zero-padded.  With
  *           B_s = sum_{s'<s} ceil(n_s'/32) and Rp = 32*(ceil(rows/32) + nseg),
  *           q is [cols, Rp] with segment s in columns [32 B_s, 32 B_{s+1}),
- *           scales [cols, Rp/32]; columns past 32 B_nseg are not written.
+ *           scales [cols, Rp/32]; columns past 32 B_nseg are written as zero
+ *           codes with scale byte 0.
  * cols % 8 == 0 for axis 0. */
 int mx_quantize(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols,
                 int32_t axis, const int32_t* seg_offsets, int32_t nseg, uint8_t* q,

@@ -77,7 +77,7 @@ bool shape_supported(const FfnShape& s) {
 }
 
 int tile_bm(int prec, int64_t R, int E) {
-  return prec == MOE_F32 ? ffn_f32_bm() : prec == MOE_MXFP8 ? 128 : ffn_bf16_bm(R, E);
+  return prec == MOE_F32 ? ffn_f32_bm() : prec == MOE_MXFP8 ? ffn_mx_bm(R, E) : ffn_bf16_bm(R, E);
 }
 
 size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }

@@ -21,7 +21,7 @@
 // MFMA operand layout (32x32x16 bf16): lane l supplies A[m = l % 32][k = 8(l/32) .. +7]
 // and B[k = 8(l/32) .. +7][n = l % 32]; accumulator register r of lane l holds
 // C[8(r/4) + 4(l/32) + r%4][l % 32].
-#include "ffn_common.hpp"
+#include "gemm_common.hpp"
 
 #ifndef MOE_BIG_BK
 #define MOE_BIG_BK 64
@@ -32,16 +32,9 @@
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace gemm;
 
 constexpr int kNoSplit = 0x7FFFFFFF;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked, out of range reads 0
-
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Tile configuration: BM x BN outputs, WM x WN waves, K-step BK, LDS ring of
 // NA stages for the A tile and NB stages for the B tile (2 or 3, not both 3).
@@ -98,22 +91,6 @@ struct McOp {
   int c0;
   int k_valid;
 };
-
-// Buffer descriptor over [base, base + bytes).  Every caller passes
-// workgroup-uniform values; readfirstlane keeps the descriptor in scalar
-// registers (a descriptor in vector registers would need a loop over lanes).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  const int n = __builtin_amdgcn_readfirstlane(bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(bytes)));
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
-  void* pb = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(pb, 0, n, kRsrcWord3);
-}
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_dst, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_dst), 16, voff, 0, 0, 0);
-}
 
 // 16-byte chunk swizzles.  K-contiguous tile rows hold BK elements; a fragment
 // read has 16 lanes on 16 consecutive rows at one chunk.  M/N-contiguous tile
@@ -204,9 +181,6 @@ __device__ __forceinline__ bf16x8 frag_mc(const uint16_t* t, int col, int ks, in
   return r;
 }
 
-template <class C>
-using Acc = f32x16[C::TM][C::TN];
-
 template <bool KC>
 struct OpFor;
 template <>
@@ -288,14 +262,6 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const
 #endif
 }
 
-// Wait until at most N LDS-DMA loads of this wave are outstanding (N < 16;
-// expcnt and lgkmcnt left alone).  Loads complete in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
-}
-
 // C = A B over K = [0, K).  K-step kt of A lives in A slot kt % NA and of B in
 // B slot kt % NB.  Right after the barrier that retires step kt - 1, step
 // kt + N - 1 of each operand is issued, the 2-deep operand first; so when step
@@ -353,63 +319,6 @@ __device__ __forceinline__ void mainloop(const typename OpFor<AKC>::T& aop, cons
   __syncthreads();  // the epilogue reuses the LDS
 }
 
-// ---------------------------------------------------------------------------
-// Epilogue through LDS: accumulators -> bf16 tile in LDS -> 16-byte stores.
-// ---------------------------------------------------------------------------
-template <class C>
-__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * C::WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-}
-template <class C>
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * C::WTN + j * 32 + (lane & 31);
-}
-
-// Copy a rows x cols bf16 tile from LDS (row stride ldc) to global memory with
-// 16-byte stores; only rows < rows_valid and columns < cols_valid are written.
-template <class C>
-__device__ __forceinline__ void flush_tile(const uint16_t* ct, int ldc, int rows, int cols, uint16_t* dst,
-                                           int64_t ld, int rows_valid, int cols_valid, int tid) {
-  const int cpr = cols / 8;
-  for (int c = tid; c < rows * cpr; c += C::kThreads) {
-    const int r = c / cpr, cc = (c % cpr) * 8;
-    if (r < rows_valid && cc < cols_valid)
-      *reinterpret_cast<uint4*>(dst + r * ld + cc) = *reinterpret_cast<const uint4*>(ct + r * ldc + cc);
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void load_tile(uint16_t* ct, int ldc, int rows, int cols, const uint16_t* src, int64_t ld,
-                                          int rows_valid, int cols_valid, int tid) {
-  const int cpr = cols / 8;
-  for (int c = tid; c < rows * cpr; c += C::kThreads) {
-    const int r = c / cpr, cc = (c % cpr) * 8;
-    const uint4 v = (r < rows_valid && cc < cols_valid) ? *reinterpret_cast<const uint4*>(src + r * ld + cc)
-                                                        : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(ct + r * ldc + cc) = v;
-  }
-}
-
-// Store the plain accumulator tile (bf16) to dst[r*ld + c].
-template <class C>
-__device__ __forceinline__ void store_acc(const Acc<C>& acc, uint16_t* lds, uint16_t* dst, int64_t ld,
-                                          int rows_valid, int cols_valid, int tid) {
-  constexpr int ldc = C::BN + 8;
-  static_assert(C::BM * ldc <= C::kLds, "output tile exceeds LDS");
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        lds[acc_row<C>(wm, i, r, lane) * ldc + acc_col<C>(wn, j, lane)] =
-            static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
-  __syncthreads();
-  flush_tile<C>(lds, ldc, C::BM, C::BN, dst, ld, rows_valid, cols_valid, tid);
-}
-
 template <class C, int KIND>
 __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLds];
@@ -442,85 +351,19 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
       const KcOp a{X + row0 * d, nullptr, d, kNoSplit, rows};
       const McOp b{Wg + e * wsz, Wu + e * wsz, f, n0, d};
       mainloop<C, true, false, true>(a, b, d, lds, tid, acc);
-      // Hg and Hu tiles (BM x BN/2 each), then A in the Hg buffer
-      constexpr int ldh = C::BN / 2 + 8;
-      static_assert(2 * C::BM * ldh <= C::kLds, "G1 epilogue tiles exceed LDS");
-      uint16_t* tg = lds;
-      uint16_t* tu = lds + C::BM * ldh;
-      const int64_t o0 = row0 * f + n0;
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN / 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int o = acc_row<C>(wm, i, r, lane) * ldh + wn * (C::WTN / 2) + j * 32 + (lane & 31);
-            tg[o] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
-            tu[o] = static_cast<uint16_t>(f32_to_bf16(acc[i][j + C::TN / 2][r]));
-          }
-      __syncthreads();
-      flush_tile<C>(tg, ldh, C::BM, C::BN / 2, static_cast<uint16_t*>(p.o_hg) + o0, f, rows, f - n0, tid);
-      flush_tile<C>(tu, ldh, C::BM, C::BN / 2, static_cast<uint16_t*>(p.o_hu) + o0, f, rows, f - n0, tid);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN / 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int o = acc_row<C>(wm, i, r, lane) * ldh + wn * (C::WTN / 2) + j * 32 + (lane & 31);
-            const float g = acc[i][j][r], u = acc[i][j + C::TN / 2][r];
-            tg[o] = static_cast<uint16_t>(f32_to_bf16(silu_f(g) * u));
-          }
-      __syncthreads();
-      flush_tile<C>(tg, ldh, C::BM, C::BN / 2, static_cast<uint16_t*>(p.o_act) + o0, f, rows, f - n0, tid);
+      epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else if constexpr (KIND == kG2) {
       const int n0 = nt * C::BN;
       const KcOp a{static_cast<const uint16_t*>(p.act) + row0 * f, nullptr, f, kNoSplit, rows};
       const McOp b{Wd + e * wsz, nullptr, d, n0, f};
       mainloop<C, true, false, false>(a, b, f, lds, tid, acc);
-      store_acc<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
+      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
       const int n0 = nt * C::BN;  // over f
       const KcOp a{static_cast<const uint16_t*>(p.dy) + row0 * d, nullptr, d, kNoSplit, rows};
       const KcOp b{Wd + e * wsz + static_cast<int64_t>(n0) * d, nullptr, d, kNoSplit, f - n0};
       mainloop<C, true, true, false>(a, b, d, lds, tid, acc);
-      // SwiGLU backward: stage Hg, Hu with 16-byte loads, compute dHg, dHu in
-      // place, 16-byte stores.  When both full tiles do not fit in LDS the tile
-      // is processed in two row halves, each by the waves owning those rows.
-      constexpr int ldc = C::BN + 8;
-      constexpr int halves = (2 * C::BM * ldc <= C::kLds) ? 1 : 2;
-      constexpr int hr = C::BM / halves;
-      static_assert(2 * hr * ldc <= C::kLds, "G3 epilogue tiles exceed LDS");
-      static_assert(halves == 1 || C::WM == 2, "the half split assumes two wave rows");
-      uint16_t* tg = lds;
-      uint16_t* tu = lds + hr * ldc;
-      for (int h = 0; h < halves; ++h) {
-        const int64_t o0 = (row0 + h * hr) * f + n0;
-        const int rv = rows - h * hr;
-        load_tile<C>(tg, ldc, hr, C::BN, static_cast<const uint16_t*>(p.hg) + o0, f, rv, f - n0, tid);
-        load_tile<C>(tu, ldc, hr, C::BN, static_cast<const uint16_t*>(p.hu) + o0, f, rv, f - n0, tid);
-        __syncthreads();
-        if (halves == 1 || wm == h) {
-#pragma unroll
-          for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int o = (acc_row<C>(wm, i, r, lane) - h * hr) * ldc + acc_col<C>(wn, j, lane);
-                const float g = bf16_to_f32(tg[o]), u = bf16_to_f32(tu[o]);
-                const float da = acc[i][j][r];
-                const float sg = sigmoid_f(g);
-                tu[o] = static_cast<uint16_t>(f32_to_bf16(da * g * sg));
-                tg[o] = static_cast<uint16_t>(f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg))));
-              }
-        }
-        __syncthreads();
-        flush_tile<C>(tg, ldc, hr, C::BN, static_cast<uint16_t*>(p.o_dhg) + o0, f, rv, f - n0, tid);
-        flush_tile<C>(tu, ldc, hr, C::BN, static_cast<uint16_t*>(p.o_dhu) + o0, f, rv, f - n0, tid);
-        __syncthreads();
-      }
+      epi_swiglu_bwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else {  // kG5
       const int n0 = nt * C::BN;  // over d
       const KcOp a{static_cast<const uint16_t*>(p.dhg) + row0 * f, static_cast<const uint16_t*>(p.dhu) + row0 * f, f,
@@ -528,7 +371,7 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
       const KcOp b{Wg + e * wsz + static_cast<int64_t>(n0) * f, Wu + e * wsz + static_cast<int64_t>(n0) * f, f, f,
                    d - n0};
       mainloop<C, true, true, false>(a, b, 2 * f, lds, tid, acc);
-      store_acc<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
+      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
     }
   } else {  // weight gradients: K = rows of expert e
     // logical tile = (expert, M tile, N tile), blocks of tiles sharing operand
@@ -563,7 +406,7 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
       nvalid = f;
     }
     mainloop<C, false, false, false>(a, b, K, lds, tid, acc);
-    store_acc<C>(acc, lds, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0, tid);
+    epi_store<C>(acc, lds, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0, tid);
   }
 }
 

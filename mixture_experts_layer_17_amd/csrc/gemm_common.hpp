@@ -1,0 +1,198 @@
+// Shared pieces of the grouped expert-FFN GEMMs (internal): the gfx950 LDS-DMA
+// load helpers and the LDS-staged epilogues.  A tile configuration C provides
+// BM x BN outputs per workgroup over WM x WN waves of WTM x WTN (TM x TN MFMA
+// tiles of 32 x 32 each), kThreads, and kLds (bf16 elements of LDS).
+//
+// Accumulator layout of the 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16 and
+// v_mfma_scale_f32_32x32x64_f8f6f4 alike): register r of lane l holds
+// C[8(r/4) + 4(l/32) + r%4][l % 32].
+#pragma once
+
+#include "ffn_common.hpp"
+
+namespace moe {
+namespace gemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked, out of range reads 0
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <class C>
+using Acc = f32x16[C::TM][C::TN];
+
+// Buffer descriptor over [base, base + bytes).  Every caller passes
+// workgroup-uniform values; readfirstlane keeps the descriptor in scalar
+// registers (a descriptor in vector registers would need a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int n = __builtin_amdgcn_readfirstlane(bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(bytes)));
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  void* pb = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pb, 0, n, kRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_dst), 16, voff, 0, 0, 0);
+}
+
+// Wait until at most N LDS-DMA loads of this wave are outstanding (N < 16;
+// expcnt and lgkmcnt left alone).  Loads complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue through LDS: accumulators -> bf16 tile in LDS -> 16-byte stores.
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
+  return wm * C::WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+template <class C>
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
+  return wn * C::WTN + j * 32 + (lane & 31);
+}
+
+// Copy a rows x cols bf16 tile from LDS (row stride ldc) to global memory with
+// 16-byte stores; only rows < rows_valid and columns < cols_valid are written.
+template <class C>
+__device__ __forceinline__ void flush_tile(const uint16_t* ct, int ldc, int rows, int cols, uint16_t* dst,
+                                           int64_t ld, int rows_valid, int cols_valid, int tid) {
+  const int cpr = cols / 8;
+  for (int c = tid; c < rows * cpr; c += C::kThreads) {
+    const int r = c / cpr, cc = (c % cpr) * 8;
+    if (r < rows_valid && cc < cols_valid)
+      *reinterpret_cast<uint4*>(dst + r * ld + cc) = *reinterpret_cast<const uint4*>(ct + r * ldc + cc);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void load_tile(uint16_t* ct, int ldc, int rows, int cols, const uint16_t* src, int64_t ld,
+                                          int rows_valid, int cols_valid, int tid) {
+  const int cpr = cols / 8;
+  for (int c = tid; c < rows * cpr; c += C::kThreads) {
+    const int r = c / cpr, cc = (c % cpr) * 8;
+    const uint4 v = (r < rows_valid && cc < cols_valid) ? *reinterpret_cast<const uint4*>(src + r * ld + cc)
+                                                        : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(ct + r * ldc + cc) = v;
+  }
+}
+
+// Store the plain accumulator tile (bf16) to dst[r*ld + c].
+template <class C>
+__device__ __forceinline__ void epi_store(const Acc<C>& acc, uint16_t* lds, uint16_t* dst, int64_t ld,
+                                          int rows_valid, int cols_valid, int tid) {
+  constexpr int ldc = C::BN + 8;
+  static_assert(C::BM * ldc <= C::kLds, "output tile exceeds LDS");
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        lds[acc_row<C>(wm, i, r, lane) * ldc + acc_col<C>(wn, j, lane)] =
+            static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
+  __syncthreads();
+  flush_tile<C>(lds, ldc, C::BM, C::BN, dst, ld, rows_valid, cols_valid, tid);
+}
+
+// G1 epilogue: Hg and Hu tiles (BM x BN/2 each: the gate columns are
+// accumulator tiles j < TN/2, the up columns j >= TN/2), then A = silu(Hg) * Hu
+// (SwiGLU) in the Hg buffer; all three stored as bf16.
+template <class C>
+__device__ __forceinline__ void epi_swiglu_fwd(const Acc<C>& acc, uint16_t* lds, const FfnArgs& p, int64_t row0,
+                                               int rows, int n0, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int f = p.f;
+  constexpr int ldh = C::BN / 2 + 8;
+  static_assert(2 * C::BM * ldh <= C::kLds, "G1 epilogue tiles exceed LDS");
+  uint16_t* tg = lds;
+  uint16_t* tu = lds + C::BM * ldh;
+  const int64_t o0 = row0 * f + n0;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN / 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = acc_row<C>(wm, i, r, lane) * ldh + wn * (C::WTN / 2) + j * 32 + (lane & 31);
+        tg[o] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
+        tu[o] = static_cast<uint16_t>(f32_to_bf16(acc[i][j + C::TN / 2][r]));
+      }
+  __syncthreads();
+  flush_tile<C>(tg, ldh, C::BM, C::BN / 2, static_cast<uint16_t*>(p.o_hg) + o0, f, rows, f - n0, tid);
+  flush_tile<C>(tu, ldh, C::BM, C::BN / 2, static_cast<uint16_t*>(p.o_hu) + o0, f, rows, f - n0, tid);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN / 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = acc_row<C>(wm, i, r, lane) * ldh + wn * (C::WTN / 2) + j * 32 + (lane & 31);
+        const float g = acc[i][j][r], u = acc[i][j + C::TN / 2][r];
+        tg[o] = static_cast<uint16_t>(f32_to_bf16(silu_f(g) * u));
+      }
+  __syncthreads();
+  flush_tile<C>(tg, ldh, C::BM, C::BN / 2, static_cast<uint16_t*>(p.o_act) + o0, f, rows, f - n0, tid);
+}
+
+// G3 epilogue: SwiGLU backward from dA (the accumulators) and the stored Hg, Hu:
+// dHu = dA * silu(Hg), dHg = dA * Hu * silu'(Hg), stored as bf16.
+template <class C>
+__device__ __forceinline__ void epi_swiglu_bwd(const Acc<C>& acc, uint16_t* lds, const FfnArgs& p, int64_t row0,
+                                               int rows, int n0, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int f = p.f;
+  // Stage Hg, Hu with 16-byte loads, compute dHg, dHu in
+  // place, 16-byte stores.  When both full tiles do not fit in LDS the tile
+  // is processed in two row halves, each by the waves owning those rows.
+  constexpr int ldc = C::BN + 8;
+  constexpr int halves = (2 * C::BM * ldc <= C::kLds) ? 1 : 2;
+  constexpr int hr = C::BM / halves;
+  static_assert(2 * hr * ldc <= C::kLds, "G3 epilogue tiles exceed LDS");
+  static_assert(halves == 1 || C::WM == 2, "the half split assumes two wave rows");
+  uint16_t* tg = lds;
+  uint16_t* tu = lds + hr * ldc;
+  for (int h = 0; h < halves; ++h) {
+    const int64_t o0 = (row0 + h * hr) * f + n0;
+    const int rv = rows - h * hr;
+    load_tile<C>(tg, ldc, hr, C::BN, static_cast<const uint16_t*>(p.hg) + o0, f, rv, f - n0, tid);
+    load_tile<C>(tu, ldc, hr, C::BN, static_cast<const uint16_t*>(p.hu) + o0, f, rv, f - n0, tid);
+    __syncthreads();
+    if (halves == 1 || wm == h) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int o = (acc_row<C>(wm, i, r, lane) - h * hr) * ldc + acc_col<C>(wn, j, lane);
+            const float g = bf16_to_f32(tg[o]), u = bf16_to_f32(tu[o]);
+            const float da = acc[i][j][r];
+            const float sg = sigmoid_f(g);
+            tu[o] = static_cast<uint16_t>(f32_to_bf16(da * g * sg));
+            tg[o] = static_cast<uint16_t>(f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg))));
+          }
+    }
+    __syncthreads();
+    flush_tile<C>(tg, ldc, hr, C::BN, static_cast<uint16_t*>(p.o_dhg) + o0, f, rv, f - n0, tid);
+    flush_tile<C>(tu, ldc, hr, C::BN, static_cast<uint16_t*>(p.o_dhu) + o0, f, rv, f - n0, tid);
+    __syncthreads();
+  }
+}
+
+}  // namespace gemm
+}  // namespace moe

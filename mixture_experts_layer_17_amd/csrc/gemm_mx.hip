@@ -7,174 +7,212 @@
 // Every GEMM operand is quantised on the device (mx.hip) along that GEMM's
 // contraction axis into a K-contiguous layout (activations: row blocks; forward
 // weights and the token-axis operands of the weight gradients: column blocks
-// stored transposed), so a single "A[m][k] * B[n][k]" kernel serves all six
+// stored transposed), so one "A[m][k] * B[n][k]" main loop serves all six
 // products.  The token-axis operands are padded to 32 tokens per expert
-// segment (block offsets from the routing metadata); their K range is masked at
-// segment ends.
+// segment (block offsets from the routing metadata).
 //
-// Tile: 128 x 128 outputs per workgroup, 4 waves of 64 x 64, K step 128 bytes
-// (two MFMA K-steps of 64).  LDS rows are 128 bytes + 16 of padding; each row's
-// four E8M0 scales of the K step sit in a 32-bit LDS word.  MFMA operand layout
-// (32x32x64 f8, checked on the hardware): lane l = (g = l/32, m = l%32) supplies
-// A[m][16g .. 16g+15] in its first 16 bytes and A[m][32+16g .. 32+16g+15] in
-// its last 16; its scale operand is the E8M0 scale of row m, block g (k in
-// [32g, 32g+32)).  B is laid out the same way with n = l % 32.
+// The fp8 tiles (K-step of 128 bytes per row) move into LDS with the gfx950
+// LDS-DMA buffer loads, 16-byte chunks XOR-swizzled by row as in the bf16
+// kernels; the E8M0 scales (one 32-bit word of four blocks per tile row and
+// K-step) are fetched one K-step ahead, one tile row per thread, and staged in LDS.  Where a K-step runs past the end of an
+// expert's token range both operands' scales are set to 2^-127, so whatever
+// finite codes lie there contribute exactly zero (products below 2^-200).
+// MFMA operand layout (32x32x64 f8, checked on the hardware): lane l =
+// (g = l/32, m = l%32) supplies A[m][16g .. 16g+15] in its first 16 bytes and
+// A[m][32+16g .. 32+16g+15] in its last 16; its scale operand is the E8M0 scale
+// of row m, block g (k in [32g, 32g+32)).  B is laid out the same way with
+// n = l % 32; the accumulators are laid out as in the bf16 kernels.
+#include "gemm_common.hpp"
 #include "mx_common.hpp"
 
 namespace moe {
 namespace {
+using namespace gemm;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;  // kBK in fp8 elements (bytes)
-constexpr int kWM = 2, kWN = 2;
-constexpr int kThreads = 64 * kWM * kWN;
-constexpr int kLd = kBK + 16;  // LDS row stride in bytes
-constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;
-constexpr int kTM = kWTM / 32, kTN = kWTN / 32;
 constexpr int kNoSplit = 0x7FFFFFFF;
 
-// K-contiguous fp8 operand with block scales: element (mn, k) at q[mn*ld + k],
-// scale of (mn, k) at s[mn*(ld/32) + k/32].  k >= ksplit reads the second
-// matrix at k - ksplit.  `dual` maps the tile's N index onto two matrices in
-// groups of kWTN/2 rows (gate and up columns side by side in every wave).
-struct MxOp {
+// Tile configuration: BM x BN outputs, WM x WN waves; K-step BK = 128 fp8
+// elements (two MFMA K-slices); two LDS stages per operand.
+template <int BM_, int BN_, int WM_, int WN_>
+struct MxCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int BK = 128;
+  static constexpr int kA = BM * BK, kB = BN * BK;  // bytes per stage
+  static constexpr int kScales = 2 * (BM + BN) * 4;   // two stages of one scale word per tile row
+  static constexpr int kEpi = cmax(2 * BM * (BN / 2 + 8), BM * (BN + 8));  // bf16 elements
+  static constexpr int kLds = cmax((2 * kA + 2 * kB + kScales) / 2, kEpi);  // bf16 elements
+  static_assert(kLds * 2 <= 160 * 1024, "LDS budget");
+  static_assert(BM + BN == kThreads, "one thread per tile row fetches the scales");
+};
+using MxBig = MxCfg<256, 256, 2, 4>;
+using MxSmall = MxCfg<128, 128, 2, 2>;
+
+// K-contiguous fp8 operand with block scales: element (mn, k) at
+// q[mn*ld + k_base + k], its scale at s[mn*(ld/32) + (k_base + k)/32]; k >=
+// ksplit reads the second matrix at k - ksplit.  Dual operands (template flag)
+// take tile rows [0, W/2) from the first matrix and [W/2, W) from the second.
+// Rows mn >= mn_valid (of each matrix) read as zero; K elements past k_valid
+// get zero-weight scales.
+struct MxKc {
   const uint8_t* q0;
   const uint8_t* q1;
   const uint8_t* s0;
   const uint8_t* s1;
-  int64_t ld;      // elements per row (a multiple of 32)
-  int64_t k_base;  // first K element of this problem inside each row
-  int k_valid;     // K elements of this problem
+  int64_t ld;      // elements (bytes) per row, a multiple of 32
+  int64_t k_base;  // first K element of this problem inside each row (multiple of 32)
+  int k_valid;     // K elements of this problem (multiple of 32)
   int ksplit;
   int mn_valid;
-  bool dual;
-  __device__ void row_of(int mn, int k, const uint8_t*& q, const uint8_t*& s, int& row, int& kk) const {
-    const bool second = dual ? ((mn % kWTN) >= kWTN / 2) : (k >= ksplit);
-    row = dual ? (mn / kWTN) * (kWTN / 2) + mn % (kWTN / 2) : mn;
-    kk = (!dual && k >= ksplit) ? k - ksplit : k;
-    q = second ? q1 : q0;
-    s = second ? s1 : s0;
-  }
 };
 
-struct MxLoader {
-  static constexpr int kChunks = 128 * kBK / 16 / kThreads;  // 16-byte chunks per thread (4)
-  uint4 v[kChunks];
-  uint32_t sc;  // four scale bytes of one row (threads < 128)
-  __device__ void load(const MxOp& op, int k0, int tid) {
+// LDS-DMA loads of a ROWS x 128-byte tile (K-step at k0).
+template <class C, int ROWS, bool DUAL>
+__device__ __forceinline__ void mx_dma(const MxKc& op, int k0, uint8_t* dst, int wave, int lane) {
+  constexpr int NI = ROWS / 8;  // 8 rows of 128 bytes per 1 KB instruction
+  static_assert(NI % C::kWaves == 0, "tile does not split over the waves");
+  const bool hi = !DUAL && k0 >= op.ksplit;
+  const int64_t kk = op.k_base + (hi ? k0 - op.ksplit : k0);
+  const int rl = lane >> 3, ph = lane & 7;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * kThreads;
-      const int mn = c / (kBK / 16), kc = (c % (kBK / 16)) * 16;
-      const uint8_t *q, *s;
-      int row, kk;
-      op.row_of(mn, k0 + kc, q, s, row, kk);
-      const bool ok = row < op.mn_valid && k0 + kc < op.k_valid;
-      v[i] = ok ? *reinterpret_cast<const uint4*>(q + row * op.ld + op.k_base + kk) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < NI / C::kWaves; ++u) {
+    const int i = wave + u * C::kWaves;
+    int row = i * 8 + rl;
+    const uint8_t* q = hi ? op.q1 : op.q0;
+    if constexpr (DUAL) {
+      if (i >= NI / 2) q = op.q1;
+      row -= (i >= NI / 2) ? ROWS / 2 : 0;
     }
-    sc = 0;
-    if (tid < 128) {
-      const uint8_t *q, *s;
-      int row, kk;
-      op.row_of(tid, k0, q, s, row, kk);
-      if (row < op.mn_valid) {
-        const uint8_t* sp = s + row * (op.ld / 32) + (op.k_base + kk) / 32;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (k0 + 32 * j < op.k_valid) sc |= static_cast<uint32_t>(sp[j]) << (8 * j);
-      }
-    }
+    const int rows = op.mn_valid < (DUAL ? ROWS / 2 : ROWS) ? op.mn_valid : (DUAL ? ROWS / 2 : ROWS);
+    // [q + kk, q + rows*ld): ends with the last valid row
+    const __amdgpu_buffer_rsrc_t r = rsrc(q + kk, static_cast<int64_t>(rows) * op.ld - kk);
+    const int lc = ph ^ ((i * 8 + rl) >> 1 & 7);
+    dma16(r, dst + i * 1024, static_cast<int>(row * op.ld + lc * 16));
   }
-  __device__ void store(uint8_t* lds, uint32_t* lds_s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * kThreads;
-      const int mn = c / (kBK / 16), kc = (c % (kBK / 16)) * 16;
-      *reinterpret_cast<uint4*>(lds + mn * kLd + kc) = v[i];
+}
+
+// The four scale bytes (blocks 0..3 of the K-step at k0) of tile row `row`,
+// byte j = block j; 0 (2^-127) past the valid rows or K range.  One dword load
+// when the row's scales for the step are 4-byte aligned, else four byte loads.
+template <bool DUAL, int ROWS>
+__device__ __forceinline__ uint32_t mx_scale_word(const MxKc& op, int row, int k0) {
+  const uint8_t* s = op.s0;
+  int r = row;
+  int kk = k0;
+  if constexpr (DUAL) {
+    if (row >= ROWS / 2) {
+      s = op.s1;
+      r = row - ROWS / 2;
     }
-    if (tid < 128) lds_s[tid] = sc;
+  } else if (k0 >= op.ksplit) {
+    s = op.s1;
+    kk = k0 - op.ksplit;
   }
-};
+  if (r >= op.mn_valid) return 0u;
+  const int64_t sld = op.ld / 32;
+  const uint8_t* p = s + r * sld + (op.k_base + kk) / 32;
+  const int nb = (op.k_valid - k0) / 32;  // valid blocks in this step (may exceed 4)
+  if (nb >= 4 && ((reinterpret_cast<uintptr_t>(p) & 3) == 0)) return *reinterpret_cast<const uint32_t*>(p);
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < nb) w |= static_cast<uint32_t>(p[j]) << (8 * j);
+  return w;
+}
 
-struct Smem {
-  uint8_t a[2][kBM * kLd];
-  uint8_t b[2][kBN * kLd];
-  uint32_t sa[2][kBM];
-  uint32_t sb[2][kBN];
-};
-
-__device__ __forceinline__ i32x8 frag(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 32);
+// One fp8 MFMA operand (32 bytes) from a 128-byte-row tile: row `row`, K-slice ks.
+__device__ __forceinline__ i32x8 mx_frag(const uint8_t* t, int row, int ks, int g) {
+  const int sw = (row >> 1) & 7;
+  const uint4 lo = *reinterpret_cast<const uint4*>(t + row * 128 + (((ks * 4 + g) ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(t + row * 128 + (((ks * 4 + 2 + g) ^ sw) << 4));
   i32x8 v;
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
 }
 
-__device__ __forceinline__ void mx_step(const Smem& sm, int buf, int wm, int wn, int lane, f32x16 (&acc)[kTM][kTN]) {
-#pragma unroll
-  for (int ks = 0; ks < kBK / 64; ++ks) {
-    i32x8 a[kTM], b[kTN];
-    int sa[kTM], sb[kTN];
-    // lane l = (g = l/32, row l%32): bytes k = 16g..16g+15 and 32+16g..32+16g+15
-    // of this 64-wide K step; its scale operand is the row's block g.
-    const int kof = ks * 64 + (lane >> 5) * 16;
-    const int sh = 8 * (ks * 2 + (lane >> 5));
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const int r = wm * kWTM + i * 32 + (lane & 31);
-      a[i] = frag(sm.a[buf] + r * kLd + kof);
-      sa[i] = static_cast<int>((sm.sa[buf][r] >> sh) & 0xFFu);
-    }
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int r = wn * kWTN + j * 32 + (lane & 31);
-      b[j] = frag(sm.b[buf] + r * kLd + kof);
-      sb[j] = static_cast<int>((sm.sb[buf][r] >> sh) & 0xFFu);
-    }
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+// B tile row of fragment j of wave column wn (dual: gate rows first, up rows at BN/2).
+template <class C, bool DUAL>
+__device__ __forceinline__ int b_row(int wn, int j) {
+  if constexpr (DUAL) {
+    constexpr int H = C::TN / 2;
+    return (j >= H ? C::BN / 2 : 0) + wn * (C::WTN / 2) + (j % H) * 32;
+  } else {
+    return wn * C::WTN + j * 32;
   }
 }
 
-__device__ __forceinline__ void mx_mainloop(const MxOp& aop, const MxOp& bop, int K, Smem& sm, int tid,
-                                            f32x16 (&acc)[kTM][kTN]) {
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / kWN, wn = wave % kWN;
+// C = A B^T over K = [0, K), both operands K-contiguous fp8 with block scales.
+// Thread t fetches the scale word of tile row t (A rows, then B rows) for the
+// next K-step while the current one is consumed, and parks it in the LDS slot
+// of that step; the lanes read their own rows' words from there.
+template <class C, bool BDUAL>
+__device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, int K, uint8_t* lds, int tid,
+                                            Acc<C>& acc) {
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j)
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nk = (K + kBK - 1) / kBK;
+  const int nk = (K + C::BK - 1) / C::BK;
   if (nk == 0) return;
-  MxLoader la, lb;
-  la.load(aop, 0, tid);
-  lb.load(bop, 0, tid);
-  la.store(sm.a[0], sm.sa[0], tid);
-  lb.store(sm.b[0], sm.sb[0], tid);
-  __syncthreads();
+  uint8_t* qa = lds;                                          // A stages
+  uint8_t* qb = lds + 2 * C::kA;                              // B stages
+  uint32_t* sw = reinterpret_cast<uint32_t*>(lds + 2 * C::kA + 2 * C::kB);  // [2][BM + BN] scale words
+  auto issue = [&](int kt) {
+    mx_dma<C, C::BM, false>(aop, kt * C::BK, qa + (kt & 1) * C::kA, wave, lane);
+    mx_dma<C, C::BN, BDUAL>(bop, kt * C::BK, qb + (kt & 1) * C::kB, wave, lane);
+  };
+  auto fetch = [&](int kt) -> uint32_t {
+    return tid < C::BM ? mx_scale_word<false, C::BM>(aop, tid, kt * C::BK)
+                       : mx_scale_word<BDUAL, C::BN>(bop, tid - C::BM, kt * C::BK);
+  };
+  issue(0);
+  sw[tid] = fetch(0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(aop, (kt + 1) * kBK, tid);
-      lb.load(bop, (kt + 1) * kBK, tid);
-    }
-    mx_step(sm, cur, wm, wn, lane, acc);
-    if (more) {
-      la.store(sm.a[cur ^ 1], sm.sa[cur ^ 1], tid);
-      lb.store(sm.b[cur ^ 1], sm.sb[cur ^ 1], tid);
-    }
+    wait_vm<0>();
     __syncthreads();
+    uint32_t next = 0;
+    if (kt + 1 < nk) {
+      issue(kt + 1);
+      next = fetch(kt + 1);
+    }
+    const uint8_t* as = qa + (kt & 1) * C::kA;
+    const uint8_t* bs = qb + (kt & 1) * C::kB;
+    const uint32_t* ss = sw + (kt & 1) * (C::BM + C::BN);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // lane (g, m): scale of block 2 ks + g of its row (byte 2 ks + g of the row's word)
+      const int sh = 8 * (2 * ks + g);
+      uint32_t ca[C::TM], cb[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) ca[i] = ss[wm * C::WTM + i * 32 + (lane & 31)];
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) cb[j] = ss[C::BM + b_row<C, BDUAL>(wn, j) + (lane & 31)];
+      i32x8 a[C::TM], b[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) a[i] = mx_frag(as, wm * C::WTM + i * 32 + (lane & 31), ks, g);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) b[j] = mx_frag(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a[i], b[j], acc[i][j], 0, 0, 0, static_cast<int>((ca[i] >> sh) & 0xFFu), 0,
+              static_cast<int>((cb[j] >> sh) & 0xFFu));
+    }
+    if (kt + 1 < nk) sw[((kt + 1) & 1) * (C::BM + C::BN) + tid] = next;
   }
+  __syncthreads();  // the epilogue reuses the LDS
 }
 
 // Quantised operands of one FFN call (device pointers into the scratch area).
@@ -187,181 +225,129 @@ struct MxArgs {
   const uint8_t *xtq, *xts, *dytq, *dyts, *atq, *ats, *dhgtq, *dhgts, *dhutq, *dhuts;  // [cols, ldt]
 };
 
-template <int KIND>
-__global__ __launch_bounds__(kThreads) void ffn_mx_kernel(MxArgs m) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+template <class C, int KIND>
+__global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLds];
+  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
   const FfnArgs& p = m.f;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / kWN, wn = wave % kWN;
+  const int tid = threadIdx.x;
   const int d = p.d, f = p.f;
   const int64_t wsz = static_cast<int64_t>(d) * f;
-  f32x16 acc[kTM][kTN];
+  Acc<C> acc;
 
   if constexpr (KIND == kG1 || KIND == kG2 || KIND == kG3 || KIND == kG5) {
-    const int4 t = p.tiles[blockIdx.y];
+    const int gx = KIND == kG1 ? (f + C::BN / 2 - 1) / (C::BN / 2)
+                               : KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
+    const int64_t lid = xcd_tile(blockIdx.x, static_cast<int64_t>(p.tiles[p.max_tiles].x) * gx);
+    if (lid < 0) return;
+    const int4 t = p.tiles[lid / gx];
     if (t.x < 0) return;
-    const int e = t.x, rows = t.z;
-    const int64_t row0 = t.y;
+    const int e = __builtin_amdgcn_readfirstlane(t.x), rows = __builtin_amdgcn_readfirstlane(t.z);
+    const int64_t row0 = __builtin_amdgcn_readfirstlane(t.y);
+    const int nt = static_cast<int>(lid % gx);
     if constexpr (KIND == kG1) {
-      const int n0 = blockIdx.x * (kBN / 2);
-      const MxOp a{m.xq + row0 * d, nullptr, m.xs + row0 * (d / 32), nullptr, d, 0, d, kNoSplit, rows, false};
-      const MxOp b{m.wgq + e * wsz + static_cast<int64_t>(n0) * d, m.wuq + e * wsz + static_cast<int64_t>(n0) * d,
-                   m.wgs + (e * wsz + static_cast<int64_t>(n0) * d) / 32,
-                   m.wus + (e * wsz + static_cast<int64_t>(n0) * d) / 32, d, 0, d, kNoSplit, f - n0, true};
-      mx_mainloop(a, b, d, sm, tid, acc);
-      uint16_t* Hg = static_cast<uint16_t*>(p.o_hg);
-      uint16_t* Hu = static_cast<uint16_t*>(p.o_hu);
-      uint16_t* A = static_cast<uint16_t*>(p.o_act);
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN / 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = n0 + wn * (kWTN / 2) + j * 32 + (lane & 31);
-            if (rl < rows && col < f) {
-              const float g = acc[i][j][r], u = acc[i][j + kTN / 2][r];
-              const int64_t o = (row0 + rl) * f + col;
-              Hg[o] = static_cast<uint16_t>(f32_to_bf16(g));
-              Hu[o] = static_cast<uint16_t>(f32_to_bf16(u));
-              A[o] = static_cast<uint16_t>(f32_to_bf16(silu_f(g) * u));
-            }
-          }
+      const int n0 = nt * (C::BN / 2);
+      const MxKc a{m.xq + row0 * d, nullptr, m.xs + row0 * (d / 32), nullptr, d, 0, d, kNoSplit, rows};
+      const int64_t wo = e * wsz + static_cast<int64_t>(n0) * d;  // transposed Wg, Wu: [E][f][d]
+      const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + wo / 32, m.wus + wo / 32, d, 0, d, kNoSplit, f - n0};
+      mx_mainloop<C, true>(a, b, d, lds8, tid, acc);
+      epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else if constexpr (KIND == kG2) {
-      const int n0 = blockIdx.x * kBN;  // over d
-      const MxOp a{m.aq + row0 * f, nullptr, m.as + row0 * (f / 32), nullptr, f, 0, f, kNoSplit, rows, false};
+      const int n0 = nt * C::BN;  // over d
+      const MxKc a{m.aq + row0 * f, nullptr, m.as + row0 * (f / 32), nullptr, f, 0, f, kNoSplit, rows};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * f;  // transposed Wd: [E][d][f]
-      const MxOp b{m.wdq + wo, nullptr, m.wds + wo / 32, nullptr, f, 0, f, kNoSplit, d - n0, false};
-      mx_mainloop(a, b, f, sm, tid, acc);
-      uint16_t* Y = static_cast<uint16_t*>(p.o_y);
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
-            if (rl < rows && col < d) Y[(row0 + rl) * d + col] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
-          }
+      const MxKc b{m.wdq + wo, nullptr, m.wds + wo / 32, nullptr, f, 0, f, kNoSplit, d - n0};
+      mx_mainloop<C, false>(a, b, f, lds8, tid, acc);
+      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
-      const int n0 = blockIdx.x * kBN;  // over f
-      const MxOp a{m.dyq + row0 * d, nullptr, m.dys + row0 * (d / 32), nullptr, d, 0, d, kNoSplit, rows, false};
+      const int n0 = nt * C::BN;  // over f
+      const MxKc a{m.dyq + row0 * d, nullptr, m.dys + row0 * (d / 32), nullptr, d, 0, d, kNoSplit, rows};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * d;  // natural Wd: [E][f][d]
-      const MxOp b{m.wdq + wo, nullptr, m.wds + wo / 32, nullptr, d, 0, d, kNoSplit, f - n0, false};
-      mx_mainloop(a, b, d, sm, tid, acc);
-      const uint16_t* Hg = static_cast<const uint16_t*>(p.hg);
-      const uint16_t* Hu = static_cast<const uint16_t*>(p.hu);
-      uint16_t* dHg = static_cast<uint16_t*>(p.o_dhg);
-      uint16_t* dHu = static_cast<uint16_t*>(p.o_dhu);
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
-            if (rl < rows && col < f) {
-              const int64_t o = (row0 + rl) * f + col;
-              const float g = bf16_to_f32(Hg[o]), u = bf16_to_f32(Hu[o]);
-              const float da = acc[i][j][r];
-              const float s = sigmoid_f(g);
-              dHu[o] = static_cast<uint16_t>(f32_to_bf16(da * g * s));
-              dHg[o] = static_cast<uint16_t>(f32_to_bf16(da * u * s * (1.0f + g * (1.0f - s))));
-            }
-          }
+      const MxKc b{m.wdq + wo, nullptr, m.wds + wo / 32, nullptr, d, 0, d, kNoSplit, f - n0};
+      mx_mainloop<C, false>(a, b, d, lds8, tid, acc);
+      epi_swiglu_bwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else {  // kG5
-      const int n0 = blockIdx.x * kBN;  // over d
-      const MxOp a{m.dhgq + row0 * f, m.dhuq + row0 * f, m.dhgs + row0 * (f / 32), m.dhus + row0 * (f / 32),
-                   f, 0, 2 * f, f, rows, false};
+      const int n0 = nt * C::BN;  // over d
+      const MxKc a{m.dhgq + row0 * f, m.dhuq + row0 * f, m.dhgs + row0 * (f / 32), m.dhus + row0 * (f / 32),
+                   f, 0, 2 * f, f, rows};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * f;  // natural Wg, Wu: [E][d][f]
-      const MxOp b{m.wgq + wo, m.wuq + wo, m.wgs + wo / 32, m.wus + wo / 32, f, 0, 2 * f, f, d - n0, false};
-      mx_mainloop(a, b, 2 * f, sm, tid, acc);
-      uint16_t* DX = static_cast<uint16_t*>(p.o_dx);
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
-            if (rl < rows && col < d) DX[(row0 + rl) * d + col] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
-          }
+      const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + wo / 32, m.wus + wo / 32, f, 0, 2 * f, f, d - n0};
+      mx_mainloop<C, false>(a, b, 2 * f, lds8, tid, acc);
+      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
     }
   } else {  // weight gradients: K = 32-padded token blocks of expert e
-    const int e = blockIdx.z;
-    const int64_t kb = static_cast<int64_t>(m.blk[e]) * 32;
-    const int K = (m.blk[e + 1] - m.blk[e]) * 32;
-    const int m0 = blockIdx.y * kBM;
-    uint16_t* C;
+    const int gm = KIND == kG4 ? (f + C::BM - 1) / C::BM : (d + C::BM - 1) / C::BM;
+    const int gn = KIND == kG4 ? (d + C::BN - 1) / C::BN : 2 * ((f + C::BN - 1) / C::BN);
+    int e, mt, ntile;
+    if (!wgrad_tile(blockIdx.x, p.E, gm, gn, e, mt, ntile)) return;
+    const int b0 = __builtin_amdgcn_readfirstlane(m.blk[e]);
+    const int64_t kb = static_cast<int64_t>(b0) * 32;
+    const int K = (__builtin_amdgcn_readfirstlane(m.blk[e + 1]) - b0) * 32;
+    const int m0 = mt * C::BM;
+    uint16_t* Cp;
     int n0, ldc, mvalid, nvalid;
-    MxOp a, b;
+    MxKc a, b;
     if constexpr (KIND == kG4) {  // dWd_e [f, d] = A_e^T dY_e
-      n0 = blockIdx.x * kBN;
-      a = MxOp{m.atq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.ats + static_cast<int64_t>(m0) * (m.ldt / 32),
-               nullptr, m.ldt, kb, K, kNoSplit, f - m0, false};
-      b = MxOp{m.dytq + static_cast<int64_t>(n0) * m.ldt, nullptr, m.dyts + static_cast<int64_t>(n0) * (m.ldt / 32),
-               nullptr, m.ldt, kb, K, kNoSplit, d - n0, false};
-      C = static_cast<uint16_t*>(p.o_dwd) + e * wsz;
+      n0 = ntile * C::BN;
+      a = MxKc{m.atq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.ats + static_cast<int64_t>(m0) * (m.ldt / 32),
+               nullptr, m.ldt, kb, K, kNoSplit, f - m0};
+      b = MxKc{m.dytq + static_cast<int64_t>(n0) * m.ldt, nullptr, m.dyts + static_cast<int64_t>(n0) * (m.ldt / 32),
+               nullptr, m.ldt, kb, K, kNoSplit, d - n0};
+      Cp = static_cast<uint16_t*>(p.o_dwd) + e * wsz;
       ldc = d;
       mvalid = f;
       nvalid = d;
     } else {  // kG6: dWg_e, dWu_e [d, f] = X_e^T dH_e
-      const int per = (f + kBN - 1) / kBN;
-      const int which = blockIdx.x / per;
-      n0 = (blockIdx.x % per) * kBN;
-      a = MxOp{m.xtq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.xts + static_cast<int64_t>(m0) * (m.ldt / 32),
-               nullptr, m.ldt, kb, K, kNoSplit, d - m0, false};
+      const int per = (f + C::BN - 1) / C::BN;
+      const int which = ntile / per;
+      n0 = (ntile % per) * C::BN;
+      a = MxKc{m.xtq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.xts + static_cast<int64_t>(m0) * (m.ldt / 32),
+               nullptr, m.ldt, kb, K, kNoSplit, d - m0};
       const uint8_t* bq = which ? m.dhutq : m.dhgtq;
       const uint8_t* bs = which ? m.dhuts : m.dhgts;
-      b = MxOp{bq + static_cast<int64_t>(n0) * m.ldt, nullptr, bs + static_cast<int64_t>(n0) * (m.ldt / 32), nullptr,
-               m.ldt, kb, K, kNoSplit, f - n0, false};
-      C = static_cast<uint16_t*>(which ? p.o_dwu : p.o_dwg) + e * wsz;
+      b = MxKc{bq + static_cast<int64_t>(n0) * m.ldt, nullptr, bs + static_cast<int64_t>(n0) * (m.ldt / 32), nullptr,
+               m.ldt, kb, K, kNoSplit, f - n0};
+      Cp = static_cast<uint16_t*>(which ? p.o_dwu : p.o_dwg) + e * wsz;
       ldc = f;
       mvalid = d;
       nvalid = f;
     }
-    mx_mainloop(a, b, K, sm, tid, acc);
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = m0 + wm * kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
-          if (rl < mvalid && col < nvalid)
-            C[static_cast<int64_t>(rl) * ldc + col] = static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
-        }
+    mx_mainloop<C, false>(a, b, K, lds8, tid, acc);
+    epi_store<C>(acc, lds, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0, tid);
   }
 }
 
-int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
-  const unsigned mt = static_cast<unsigned>(max_tiles);
-  const unsigned nd = static_cast<unsigned>(cdiv(a.f.d, kBN));
-  const unsigned nf = static_cast<unsigned>(cdiv(a.f.f, kBN));
-  const dim3 blk(kThreads);
+template <class C>
+int launch_mx_cfg(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
+  const int64_t nd = cdiv(a.f.d, C::BN), nf = cdiv(a.f.f, C::BN);
+  const dim3 blk(C::kThreads);
   switch (kind) {
     case kG1:
-      MOE_LAUNCH("G1_mx", ffn_mx_kernel<kG1>, dim3(static_cast<unsigned>(cdiv(a.f.f, kBN / 2)), mt), blk, 0, s, a);
+      MOE_LAUNCH("G1_mx", (ffn_mx_kernel<C, kG1>), dim3(xcd_grid(cdiv(a.f.f, C::BN / 2) * max_tiles)), blk, 0, s, a);
       break;
-    case kG2: MOE_LAUNCH("G2_mx", ffn_mx_kernel<kG2>, dim3(nd, mt), blk, 0, s, a); break;
-    case kG3: MOE_LAUNCH("G3_mx", ffn_mx_kernel<kG3>, dim3(nf, mt), blk, 0, s, a); break;
-    case kG5: MOE_LAUNCH("G5_mx", ffn_mx_kernel<kG5>, dim3(nd, mt), blk, 0, s, a); break;
+    case kG2: MOE_LAUNCH("G2_mx", (ffn_mx_kernel<C, kG2>), dim3(xcd_grid(nd * max_tiles)), blk, 0, s, a); break;
+    case kG3: MOE_LAUNCH("G3_mx", (ffn_mx_kernel<C, kG3>), dim3(xcd_grid(nf * max_tiles)), blk, 0, s, a); break;
+    case kG5: MOE_LAUNCH("G5_mx", (ffn_mx_kernel<C, kG5>), dim3(xcd_grid(nd * max_tiles)), blk, 0, s, a); break;
     case kG4:
-      MOE_LAUNCH("G4_mx", ffn_mx_kernel<kG4>, dim3(nd, static_cast<unsigned>(cdiv(a.f.f, kBM)), a.f.E), blk, 0, s,
-                 a);
+      MOE_LAUNCH("G4_mx", (ffn_mx_kernel<C, kG4>), dim3(static_cast<unsigned>(a.f.E * cdiv(a.f.f, C::BM) * nd)), blk,
+                 0, s, a);
       break;
     case kG6:
-      MOE_LAUNCH("G6_mx", ffn_mx_kernel<kG6>, dim3(2 * nf, static_cast<unsigned>(cdiv(a.f.d, kBM)), a.f.E), blk, 0,
-                 s, a);
+      MOE_LAUNCH("G6_mx", (ffn_mx_kernel<C, kG6>), dim3(static_cast<unsigned>(a.f.E * cdiv(a.f.d, C::BM) * 2 * nf)),
+                 blk, 0, s, a);
       break;
     default: return MOE_EINVAL;
   }
   return launch_status();
+}
+
+bool mx_big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 1024; }
+bool mx_big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
+
+int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
+  const bool wgrad = kind == kG4 || kind == kG6;
+  const bool big = wgrad ? mx_big_wgrad(a.f) : mx_big_rows(a.f.R, a.f.E);
+  return big ? launch_mx_cfg<MxBig>(kind, a, max_tiles, s) : launch_mx_cfg<MxSmall>(kind, a, max_tiles, s);
 }
 
 // Scratch carving: a bump allocator over the caller's workspace.
@@ -427,6 +413,8 @@ BwdBufs carve_bwd(Carve& c, int64_t R, int E, int d, int f) {
 }
 
 }  // namespace
+
+int ffn_mx_bm(int64_t R, int E) { return mx_big_rows(R, E) ? MxBig::BM : MxSmall::BM; }
 
 size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd) {
   Carve c{nullptr};

@@ -98,17 +98,22 @@ __global__ __launch_bounds__(64) void mx_cols_kernel(const T* __restrict__ src, 
       }
     }
     __syncthreads();
-    if (b >= s_blk[nseg]) return;
-    int lo = 0, hi = nseg;  // find s with s_blk[s] <= b < s_blk[s+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_blk[mid] <= b) lo = mid; else hi = mid;
+    if (b >= s_blk[nseg]) {
+      // padding past the last segment: written as zero codes with zero-block scales
+      r0 = 0;
+      nvalid = 0;
+    } else {
+      int lo = 0, hi = nseg;  // find s with s_blk[s] <= b < s_blk[s+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_blk[mid] <= b) lo = mid; else hi = mid;
+      }
+      r0 = s_off[lo] + (b - s_blk[lo]) * 32;
+      const int64_t end = s_off[lo + 1] < rows ? s_off[lo + 1] : rows;
+      nvalid = end - r0;
+      if (nvalid > 32) nvalid = 32;
+      if (nvalid < 0) nvalid = 0;
     }
-    r0 = s_off[lo] + (b - s_blk[lo]) * 32;
-    const int64_t end = s_off[lo + 1] < rows ? s_off[lo + 1] : rows;
-    nvalid = end - r0;
-    if (nvalid > 32) nvalid = 32;
-    if (nvalid < 0) nvalid = 0;
   } else {
     r0 = b * 32;
     nvalid = 32;

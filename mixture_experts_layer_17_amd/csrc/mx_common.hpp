@@ -59,6 +59,7 @@ void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows,
 
 // MXFP8 expert FFN (gemm_mx.hip).
 size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd);
+int ffn_mx_bm(int64_t R, int E);  // row-tile height for this workload
 int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, char* scratch, hipStream_t s);
 int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, char* scratch, hipStream_t s);
 

@@ -170,7 +170,11 @@ def test_mx_quantize_segments_bit_exact(gpu):
     t, v = _mx_input((500, 136), 3, torch.bfloat16)
     seg = np.array([0, 0, 45, 45, 77, 300, 301, 500], np.int32)
     nseg = len(seg) - 1
-    q, s = B.mx_quantize(t.cuda(), axis=0, seg_offsets=torch.from_numpy(seg).cuda(), nseg=nseg)
+    rp = 32 * (-(-500 // 32) + nseg)
+    # outputs pre-filled with 0xFF so that unwritten bytes show
+    q0 = torch.full((136, rp), 0xFF, dtype=torch.uint8, device="cuda")
+    s0 = torch.full((136, rp // 32), 0xFF, dtype=torch.uint8, device="cuda")
+    q, s = B.mx_quantize(t.cuda(), axis=0, seg_offsets=torch.from_numpy(seg).cuda(), nseg=nseg, q=q0, scales=s0)
     torch.cuda.synchronize()
     rq, rs = mxo.mx_quantize(v, axis=0, seg_offsets=seg)
     q, s = q.cpu().numpy(), s.cpu().numpy()
@@ -185,3 +189,4 @@ def test_mx_quantize_segments_bit_exact(gpu):
             np.testing.assert_array_equal(s[:, b], rs[b])
             b += 1
     assert b == len(rs)
+    assert np.all(q[:, 32 * b:] == 0) and np.all(s[:, b:] == 0)   # padding past the last segment
