@@ -9,9 +9,10 @@
 // block, each lane converts 8 elements; amax is combined with two lane
 // exchanges.  A wave instruction reads 1 KiB (bf16) and writes 512 bytes.
 // Column layout (blocks down the rows, written transposed so each block's 32
-// bytes are contiguous): one lane owns 16 bytes of columns for 32 rows; the 32
-// row loads of a wave are 1 KiB each.  Blocks may restart at segment
-// boundaries (expert segments of the token axis) with zero-padded tails.
+// bytes are contiguous): tiles of 4 blocks x 64 columns pass through LDS so
+// that both the row reads and the transposed writes are whole 128-byte runs.
+// Blocks may restart at segment boundaries (expert segments of the token axis)
+// with zero-padded tails.
 #include "mx_common.hpp"
 
 namespace moe {
@@ -59,35 +60,35 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const T* __restrict__ src,
   if ((i & 3) == 0) sc[i >> 2] = static_cast<uint8_t>(e + 127);
 }
 
-// j-th element (compile-time j after unrolling) of a 16-byte vector, as fp32.
-template <typename T>
-__device__ __forceinline__ float elem_of(const uint4& v, int j);
-template <>
-__device__ __forceinline__ float elem_of<uint16_t>(const uint4& v, int j) {
-  const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-  return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
-}
-template <>
-__device__ __forceinline__ float elem_of<float>(const uint4& v, int j) {
-  return __uint_as_float(j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w);
-}
+// Column layout: a workgroup takes 4 consecutive 32-row blocks (in block
+// order; with segments each block has its own first row and valid rows) x 64
+// columns.  Rows come in as 16-byte vectors into LDS; wave w quantises block w
+// with one column per lane (32 values down the column); the 64 x 128 encoded
+// bytes are staged in LDS and leave as whole 128-byte runs of output rows.
+constexpr int kColW = 64;
 
-// One wave per (32-row block, 64*VEC columns); VEC columns per lane.
 template <typename T>
-__global__ __launch_bounds__(64) void mx_cols_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
-                                                    const int32_t* __restrict__ seg, int nseg, int64_t ldq,
-                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-  constexpr int VEC = 16 / sizeof(T);
+__global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+                                                     const int32_t* __restrict__ seg, int nseg, int64_t ldq,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  constexpr int VEC = 16 / sizeof(T);       // elements per 16-byte vector
+  constexpr int VPR = kColW / VEC;          // vectors per tile row
+  constexpr int LDT = kColW + VEC;          // padded tile row (16-byte aligned)
+  __shared__ __attribute__((aligned(16))) T tile[128 * LDT];
+  __shared__ uint32_t obuf[kColW][33];      // encoded bytes: 4 blocks x 32 per output row
+  __shared__ uint8_t osc[kColW][4];
   __shared__ int32_t s_off[kMaxE + 1];
   __shared__ int32_t s_blk[kMaxE + 1];
-  const int lane = threadIdx.x;
-  const int64_t b = blockIdx.y;  // global 32-row block index
+  __shared__ int64_t b_r0[4];
+  __shared__ int b_nv[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bz = blockIdx.z;
-  int64_t r0, nvalid;
+  const int64_t nblk = seg ? ldq / 32 : rows / 32;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 4;
   if (seg) {
-    for (int i = lane; i <= nseg; i += 64) s_off[i] = seg[i];
+    for (int i = tid; i <= nseg; i += blockDim.x) s_off[i] = seg[i];
     __syncthreads();
-    if (lane == 0) {
+    if (tid == 0) {
       int32_t run = 0;
       s_blk[0] = 0;
       for (int i = 0; i < nseg; ++i) {
@@ -98,53 +99,74 @@ __global__ __launch_bounds__(64) void mx_cols_kernel(const T* __restrict__ src, 
       }
     }
     __syncthreads();
-    if (b >= s_blk[nseg]) {
-      // padding past the last segment: written as zero codes with zero-block scales
-      r0 = 0;
-      nvalid = 0;
-    } else {
-      int lo = 0, hi = nseg;  // find s with s_blk[s] <= b < s_blk[s+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_blk[mid] <= b) lo = mid; else hi = mid;
-      }
-      r0 = s_off[lo] + (b - s_blk[lo]) * 32;
-      const int64_t end = s_off[lo + 1] < rows ? s_off[lo + 1] : rows;
-      nvalid = end - r0;
-      if (nvalid > 32) nvalid = 32;
-      if (nvalid < 0) nvalid = 0;
-    }
-  } else {
-    r0 = b * 32;
-    nvalid = 32;
   }
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 64 + lane) * VEC;
-  if (c0 >= cols) return;
-  const T* base = src + bz * rows * cols + r0 * cols + c0;
-  uint4 raw[32];
-#pragma unroll
-  for (int r = 0; r < 32; ++r)
-    raw[r] = r < nvalid ? *reinterpret_cast<const uint4*>(base + r * cols) : make_uint4(0, 0, 0, 0);
-  uint8_t* qb = q + bz * cols * ldq;
-  uint8_t* sb = sc + bz * cols * (ldq / 32);
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
+  if (tid < 4) {
+    const int64_t b = b0 + tid;
+    int64_t r0 = 0, nv = 0;
+    if (b < nblk) {
+      if (!seg) {
+        r0 = b * 32;
+        nv = 32;
+      } else if (b < s_blk[nseg]) {  // blocks past the last segment stay zero padding
+        int lo = 0, hi = nseg;       // s with s_blk[s] <= b < s_blk[s+1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_blk[mid] <= b) lo = mid; else hi = mid;
+        }
+        r0 = s_off[lo] + (b - s_blk[lo]) * 32;
+        const int64_t end = s_off[lo + 1] < rows ? s_off[lo + 1] : rows;
+        nv = end - r0;
+        if (nv > 32) nv = 32;
+        if (nv < 0) nv = 0;
+      }
+    }
+    b_r0[tid] = r0;
+    b_nv[tid] = static_cast<int>(nv);
+  }
+  __syncthreads();
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kColW;
+  const T* base = src + bz * rows * cols;
+  for (int v = tid; v < 128 * VPR; v += blockDim.x) {
+    const int tr = v / VPR, cv = v - tr * VPR;
+    const int blk = tr >> 5, r = tr & 31;
+    const int64_t col = c0 + cv * VEC;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r < b_nv[blk] && col < cols) val = *reinterpret_cast<const uint4*>(base + (b_r0[blk] + r) * cols + col);
+    *reinterpret_cast<uint4*>(tile + tr * LDT + cv * VEC) = val;
+  }
+  __syncthreads();
+  {
+    float v[32];
     float amax = 0.f;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(elem_of<T>(raw[r], j)));
+    for (int r = 0; r < 32; ++r) {
+      v[r] = Elem<T>::load1(tile, (wave * 32 + r) * LDT + lane);
+      amax = fmaxf(amax, fabsf(v[r]));
+    }
     const int e = mx_block_exponent(amax);
     const float inv = mx_inv_scale(e);
-    uint32_t w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      w[k] = 0;
+      uint32_t w = 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) w[k] |= e4m3_encode(elem_of<T>(raw[4 * k + t], j) * inv) << (8 * t);
+      for (int t = 0; t < 4; ++t) w |= e4m3_encode(v[4 * k + t] * inv) << (8 * t);
+      obuf[lane][wave * 8 + k] = w;
     }
-    uint4* dst = reinterpret_cast<uint4*>(qb + (c0 + j) * ldq + b * 32);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    sb[(c0 + j) * (ldq / 32) + b] = static_cast<uint8_t>(e + 127);
+    osc[lane][wave] = static_cast<uint8_t>(e + 127);
+  }
+  __syncthreads();
+  uint8_t* qb = q + bz * cols * ldq;
+  for (int c = tid; c < kColW * 8; c += blockDim.x) {
+    const int oc = c >> 3, ch = c & 7;  // 16-byte chunk ch of output row oc (block ch / 2)
+    if (c0 + oc < cols && b0 + (ch >> 1) < nblk) {
+      const uint32_t* o = &obuf[oc][ch * 4];
+      *reinterpret_cast<uint4*>(qb + (c0 + oc) * ldq + b0 * 32 + ch * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  uint8_t* sb = sc + bz * cols * (ldq / 32);
+  {
+    const int oc = tid >> 2, j = tid & 3;
+    if (c0 + oc < cols && b0 + j < nblk) sb[(c0 + oc) * (ldq / 32) + b0 + j] = osc[oc][j];
   }
 }
 
@@ -164,17 +186,16 @@ void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, 
 
 void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
                     int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s) {
-  const int vec = src_dtype == MOE_F32 ? 4 : 8;
   const int64_t nblk = seg ? cdiv(rows, 32) + nseg : rows / 32;
   if (nblk == 0 || cols == 0 || batch == 0) return;
-  const dim3 grid(static_cast<unsigned>(cdiv(cols, 64 * vec)), static_cast<unsigned>(nblk),
+  const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
                   static_cast<unsigned>(batch));
   if (src_dtype == MOE_F32)
-    MOE_LAUNCH("mx_quantize_cols", mx_cols_kernel<float>, grid, dim3(64), 0, s, static_cast<const float*>(src), rows, cols, seg,
-                       nseg, ldq, q, sc);
+    MOE_LAUNCH("mx_quantize_cols", mx_cols_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(src), rows,
+               cols, seg, nseg, ldq, q, sc);
   else
-    MOE_LAUNCH("mx_quantize_cols", mx_cols_kernel<uint16_t>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(src), rows, cols,
-                       seg, nseg, ldq, q, sc);
+    MOE_LAUNCH("mx_quantize_cols", mx_cols_kernel<uint16_t>, grid, dim3(256), 0, s,
+               static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc);
 }
 
 }  // namespace moe
