@@ -80,6 +80,12 @@ def kernel_work(name: str, w, s: int) -> tuple[str, float]:
     }
     if name in hbm:
         return "hbm", float(hbm[name])
+    if name in ("mx_quantize_rows", "mx_quantize_cols"):
+        # per step each quantises X and dY [R, d], A, dHg, dHu [R, f] and the three weights [E, d, f] once
+        # (rows: along the contiguous axis; cols: down the rows, transposed), in 8 launches; per element
+        # the source (s bytes) is read and 1 + 1/32 bytes written
+        elems = 2 * R * d + 3 * R * f + 3 * E * d * f
+        return "hbm", float(elems * (s + 1 + 1 / 32) / 8)
     return "other", 0.0
 
 
@@ -186,7 +192,7 @@ def main() -> int:
     traffic = counted_traffic(tag, dom)
     if bound == "mfma":
         peak = PEAK[w.prec]
-        roof = {"bound": "mfma", "kernel": dom, "achieved": work / avg_s / 1e12, "peak": peak / 1e12,
+        roof = {"bound": "mfma" if w.prec != "f32" else "alu", "kernel": dom, "achieved": work / avg_s / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": work / avg_s / peak, "traffic": traffic,
                 "work_per_launch": f"{work:.4g} FLOP", "avg_launch_us": per_launch_us[dom]}
     else:
