@@ -158,17 +158,39 @@ int moe_combine_bwd(const void* dout, const void* y_perm, int dtype, const float
  * MOE_MXFP8 quantises every GEMM operand on the device to E4M3 with one E8M0
  * scale per 32 elements along that GEMM's contraction axis (as mx_quantize).
  * Limits: d % 64 == 0 and f % 64 == 0 (MOE_MXFP8: % 128).  mx_blk_offsets
- * (from moe_route_topk) is required by the MOE_MXFP8 backward, else ignored. */
+ * (from moe_route_topk) is required by the MOE_MXFP8 backward, else ignored.
+ * mx_wcache (MOE_MXFP8 only, else ignored; may be NULL): a cache built by
+ * moe_mx_weight_cache_build from these same weights, E, d and f; with it the
+ * call quantises no weight (w_gate/w_up/w_down are still passed and
+ * validated); results are bit-identical to those without it. */
 size_t moe_grouped_ffn_workspace(int64_t R, int32_t E, int32_t d, int32_t f, int prec, int is_bwd);
 int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                         const void* x_perm, const void* w_gate, const void* w_up, const void* w_down,
-                        void* h_gate, void* h_up, void* a_act, void* y_perm, void* ws,
-                        size_t ws_bytes, void* stream);
+                        const void* mx_wcache, void* h_gate, void* h_up, void* a_act, void* y_perm,
+                        void* ws, size_t ws_bytes, void* stream);
 int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                         const int32_t* mx_blk_offsets, const void* dy_perm, const void* x_perm,
                         const void* h_gate, const void* h_up, const void* a_act, const void* w_gate,
-                        const void* w_up, const void* w_down, void* dx_perm, void* dw_gate,
-                        void* dw_up, void* dw_down, void* ws, size_t ws_bytes, void* stream);
+                        const void* w_up, const void* w_down, const void* mx_wcache, void* dx_perm,
+                        void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Pre-quantised MXFP8 expert weights ("Scaling and optimizing MoE training":
+ * converting into MXFP8 has a cost the savings must exceed).  Weights change
+ * once per optimiser step, so a loop with several micro-batches per step can
+ * quantise them once: the cache holds each of w_gate, w_up [E, d, f] and
+ * w_down [E, f, d] (bf16) in both orientations the MXFP8 FFN uses (forward:
+ * blocks along d for w_gate/w_up and along f for w_down; backward: blocks along
+ * the last axis), each produced from a single read of the weight.
+ * moe_mx_weight_cache_bytes(E, d, f) = 6 E d f (1 + 1/32) bytes plus alignment;
+ * the layout is internal (hand the cache back to moe_grouped_ffn_fwd/_bwd
+ * unchanged).  The cache stays valid while the weights are unchanged; building
+ * again overwrites it.  Errors: MOE_EINVAL (null or unaligned pointer, bad E,
+ * d, f), MOE_EUNSUPPORTED (d or f not a multiple of 128), MOE_EWORKSPACE
+ * (cache_bytes too small); nothing is launched then. */
+size_t moe_mx_weight_cache_bytes(int32_t E, int32_t d, int32_t f);
+int moe_mx_weight_cache_build(const void* w_gate, const void* w_up, const void* w_down, int32_t E,
+                              int32_t d, int32_t f, void* cache, size_t cache_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * MXFP8 quantiser ("Scaling and optimizing MoE training" names MXFP8 and the

@@ -39,8 +39,10 @@ _SIGS = {
     "moe_combine_bwd": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
                                _c_void_p, _c_void_p]),
     "moe_grouped_ffn_workspace": (_sz, [_i64, _i32, _i32, _i32, _int, _int]),
-    "moe_grouped_ffn_fwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 9 + [_c_void_p, _sz, _c_void_p]),
-    "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 14 + [_c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_fwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 10 + [_c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 15 + [_c_void_p, _sz, _c_void_p]),
+    "moe_mx_weight_cache_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_mx_weight_cache_build": (_int, [_c_void_p] * 3 + [_i32, _i32, _i32, _c_void_p, _sz, _c_void_p]),
     "mx_quantize": (_int, [_c_void_p, _int, _i64, _i64, _i64, _i32, _c_void_p, _i32, _c_void_p, _c_void_p,
                            _c_void_p]),
     "moe_timing_enable": (_int, [_int]),
@@ -195,7 +197,7 @@ def moe_grouped_ffn_workspace(R, E, d, f, prec, is_bwd):
     return lib().moe_grouped_ffn_workspace(R, E, d, f, _PREC[prec], int(is_bwd))
 
 
-def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, ws=None):
+def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, ws=None, mx_wcache=None):
     R, d = x_perm.shape
     E, _, f = w_gate.shape
     dev = x_perm.device
@@ -204,13 +206,14 @@ def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, w
         out["y_perm"] = torch.empty((R, d), dtype=x_perm.dtype, device=dev)
     ws = _ws(moe_grouped_ffn_workspace(R, E, d, f, prec, 0), dev) if ws is None else ws
     _check(lib().moe_grouped_ffn_fwd(R, E, d, f, _PREC[prec], _p(offsets), _p(x_perm), _p(w_gate), _p(w_up),
-                                     _p(w_down), _p(out["h_gate"]), _p(out["h_up"]), _p(out["a_act"]),
-                                     _p(out["y_perm"]), _p(ws), ws.numel(), _stream()), "moe_grouped_ffn_fwd")
+                                     _p(w_down), _p(mx_wcache), _p(out["h_gate"]), _p(out["h_up"]),
+                                     _p(out["a_act"]), _p(out["y_perm"]), _p(ws), ws.numel(), _stream()),
+           "moe_grouped_ffn_fwd")
     return out
 
 
 def moe_grouped_ffn_bwd(dy_perm, x_perm, h_gate, h_up, a_act, offsets, mx_blk_offsets, w_gate, w_up, w_down, prec,
-                        out=None, ws=None):
+                        out=None, ws=None, mx_wcache=None):
     R, d = x_perm.shape
     E, _, f = w_gate.shape
     dev = x_perm.device
@@ -220,9 +223,19 @@ def moe_grouped_ffn_bwd(dy_perm, x_perm, h_gate, h_up, a_act, offsets, mx_blk_of
     ws = _ws(moe_grouped_ffn_workspace(R, E, d, f, prec, 1), dev) if ws is None else ws
     _check(lib().moe_grouped_ffn_bwd(R, E, d, f, _PREC[prec], _p(offsets), _p(mx_blk_offsets), _p(dy_perm),
                                      _p(x_perm), _p(h_gate), _p(h_up), _p(a_act), _p(w_gate), _p(w_up), _p(w_down),
-                                     _p(out["dx_perm"]), _p(out["dw_gate"]), _p(out["dw_up"]), _p(out["dw_down"]),
-                                     _p(ws), ws.numel(), _stream()), "moe_grouped_ffn_bwd")
+                                     _p(mx_wcache), _p(out["dx_perm"]), _p(out["dw_gate"]), _p(out["dw_up"]),
+                                     _p(out["dw_down"]), _p(ws), ws.numel(), _stream()), "moe_grouped_ffn_bwd")
     return out
+
+
+def moe_mx_weight_cache_build(w_gate, w_up, w_down, cache=None):
+    """Pre-quantised MXFP8 weights (both orientations); returns the uint8 cache tensor."""
+    E, d, f = w_gate.shape
+    n = lib().moe_mx_weight_cache_bytes(E, d, f)
+    cache = _ws(n, w_gate.device) if cache is None else cache
+    _check(lib().moe_mx_weight_cache_build(_p(w_gate), _p(w_up), _p(w_down), E, d, f, _p(cache), cache.numel(),
+                                           _stream()), "moe_mx_weight_cache_build")
+    return cache
 
 
 # --------------------------------------------------------------------------- MX quantiser

@@ -412,9 +412,46 @@ BwdBufs carve_bwd(Carve& c, int64_t R, int E, int d, int f) {
   return b;
 }
 
+// Pre-quantised weights: every weight in the forward orientation (blocks along
+// the forward GEMM's K, stored K-contiguous: Wg, Wu as [E][f][d], Wd as
+// [E][d][f]) and the backward one (natural layouts, blocks along the last axis).
+struct WCache {
+  QPair wg_f, wu_f, wd_f, wg_b, wu_b, wd_b;
+};
+
+WCache carve_wcache(Carve& c, int E, int d, int f) {
+  const int64_t w = static_cast<int64_t>(E) * d * f;
+  WCache r;
+  r.wg_f = take_q(c, w);
+  r.wu_f = take_q(c, w);
+  r.wd_f = take_q(c, w);
+  r.wg_b = take_q(c, w);
+  r.wu_b = take_q(c, w);
+  r.wd_b = take_q(c, w);
+  return r;
+}
+
 }  // namespace
 
 int ffn_mx_bm(int64_t R, int E) { return mx_big_rows(R, E) ? MxBig::BM : MxSmall::BM; }
+
+size_t mx_wcache_bytes(int E, int d, int f) {
+  Carve c{nullptr};
+  carve_wcache(c, E, d, f);
+  return c.used;
+}
+
+void mx_wcache_build(const void* wg, const void* wu, const void* wd, int E, int d, int f, char* cache,
+                     hipStream_t s) {
+  Carve c{cache};
+  const WCache w = carve_wcache(c, E, d, f);
+  const int bf = MOE_BF16;
+  // Wg, Wu [E][d][f]: along d -> [E][f][d] (forward), along f -> [E][d][f] (backward)
+  launch_mx_both(wg, bf, E, d, f, w.wg_f.q, w.wg_f.s, w.wg_b.q, w.wg_b.s, s);
+  launch_mx_both(wu, bf, E, d, f, w.wu_f.q, w.wu_f.s, w.wu_b.q, w.wu_b.s, s);
+  // Wd [E][f][d]: along f -> [E][d][f] (forward), along d -> [E][f][d] (backward)
+  launch_mx_both(wd, bf, E, f, d, w.wd_f.q, w.wd_f.s, w.wd_b.q, w.wd_b.s, s);
+}
 
 size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd) {
   Carve c{nullptr};
@@ -425,28 +462,34 @@ size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd) {
   return c.used;
 }
 
-int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, char* scratch, hipStream_t s) {
+int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* scratch, hipStream_t s) {
   Carve c{scratch};
   const FwdBufs b = carve_fwd(c, a.R, a.E, a.d, a.f);
   const int bf = MOE_BF16;
-  // X along d (rows); Wg, Wu [E][d][f] along d -> [E][f][d]; Wd [E][f][d] along f -> [E][d][f]
-  launch_mx_rows(a.x, bf, a.R, a.d, b.x.q, b.x.s, s);
-  launch_mx_cols(a.wg, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wg.q, b.wg.s, s);
-  launch_mx_cols(a.wu, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wu.q, b.wu.s, s);
-  launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s);
   MxArgs m{};
   m.f = a;
+  // X along d (rows); Wg, Wu [E][d][f] along d -> [E][f][d]; Wd [E][f][d] along f -> [E][d][f]
+  launch_mx_rows(a.x, bf, a.R, a.d, b.x.q, b.x.s, s);
+  if (wcache) {
+    Carve cc{const_cast<char*>(wcache)};
+    const WCache w = carve_wcache(cc, a.E, a.d, a.f);
+    m.wgq = w.wg_f.q; m.wgs = w.wg_f.s; m.wuq = w.wu_f.q; m.wus = w.wu_f.s; m.wdq = w.wd_f.q; m.wds = w.wd_f.s;
+  } else {
+    launch_mx_cols(a.wg, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wg.q, b.wg.s, s);
+    launch_mx_cols(a.wu, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wu.q, b.wu.s, s);
+    launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s);
+    m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s; m.wdq = b.wd.q; m.wds = b.wd.s;
+  }
   m.xq = b.x.q; m.xs = b.x.s;
-  m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s;
   int st = launch_mx_kind(kG1, m, max_tiles, s);
   if (st != MOE_OK) return st;
   launch_mx_rows(a.o_act, bf, a.R, a.f, b.a.q, b.a.s, s);
   m.aq = b.a.q; m.as = b.a.s;
-  m.wdq = b.wd.q; m.wds = b.wd.s;
   return launch_mx_kind(kG2, m, max_tiles, s);
 }
 
-int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, char* scratch, hipStream_t s) {
+int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache, char* scratch,
+               hipStream_t s) {
   Carve c{scratch};
   const BwdBufs b = carve_bwd(c, a.R, a.E, a.d, a.f);
   const int bf = MOE_BF16;
@@ -457,19 +500,29 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
   m.ldt = rp;
   int st = MOE_OK;
   if (a.R > 0) {
+    // weights in the backward orientation: natural layouts, blocks along the last axis
+    if (wcache) {
+      Carve cc{const_cast<char*>(wcache)};
+      const WCache w = carve_wcache(cc, a.E, a.d, a.f);
+      m.wdq = w.wd_b.q; m.wds = w.wd_b.s; m.wgq = w.wg_b.q; m.wgs = w.wg_b.s; m.wuq = w.wu_b.q; m.wus = w.wu_b.s;
+    } else {
+      launch_mx_rows(a.wd, bf, static_cast<int64_t>(a.E) * a.f, a.d, b.wd.q, b.wd.s, s);
+      m.wdq = b.wd.q; m.wds = b.wd.s;
+    }
     // G3: dA = dY Wd^T: dY along d, Wd natural [E][f][d] along d
     launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s);
-    launch_mx_rows(a.wd, bf, static_cast<int64_t>(a.E) * a.f, a.d, b.wd.q, b.wd.s, s);
-    m.dyq = b.dy.q; m.dys = b.dy.s; m.wdq = b.wd.q; m.wds = b.wd.s;
+    m.dyq = b.dy.q; m.dys = b.dy.s;
     st = launch_mx_kind(kG3, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f
     launch_mx_rows(a.dhg, bf, a.R, a.f, b.dhg.q, b.dhg.s, s);
     launch_mx_rows(a.dhu, bf, a.R, a.f, b.dhu.q, b.dhu.s, s);
-    launch_mx_rows(a.wg, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wg.q, b.wg.s, s);
-    launch_mx_rows(a.wu, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wu.q, b.wu.s, s);
+    if (!wcache) {
+      launch_mx_rows(a.wg, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wg.q, b.wg.s, s);
+      launch_mx_rows(a.wu, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wu.q, b.wu.s, s);
+      m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s;
+    }
     m.dhgq = b.dhg.q; m.dhgs = b.dhg.s; m.dhuq = b.dhu.q; m.dhus = b.dhu.s;
-    m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s;
     st = launch_mx_kind(kG5, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // weight gradients: every operand along tokens, per expert segment, transposed

@@ -67,10 +67,15 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const T* __restrict__ src,
 // bytes are staged in LDS and leave as whole 128-byte runs of output rows.
 constexpr int kColW = 64;
 
-template <typename T>
+// With BOTH (no segments), the same tile is also quantised along the columns:
+// thread t encodes 32 consecutive elements of tile row t/2 into the row layout
+// qr [batch, rows, cols], scr [batch, rows, cols/32] (one read of the source
+// serves both orientations).
+template <typename T, bool BOTH>
 __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
                                                      const int32_t* __restrict__ seg, int nseg, int64_t ldq,
-                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                     uint8_t* __restrict__ qr, uint8_t* __restrict__ scr) {
   constexpr int VEC = 16 / sizeof(T);       // elements per 16-byte vector
   constexpr int VPR = kColW / VEC;          // vectors per tile row
   constexpr int LDT = kColW + VEC;          // padded tile row (16-byte aligned)
@@ -168,6 +173,40 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     const int oc = tid >> 2, j = tid & 3;
     if (c0 + oc < cols && b0 + j < nblk) sb[(c0 + oc) * (ldq / 32) + b0 + j] = osc[oc][j];
   }
+  if constexpr (BOTH) {
+    // row layout: tile row tr = tid / 2, column block cb = tid % 2 (32 elements)
+    const int tr = tid >> 1, cb = tid & 1;
+    const int64_t r = b0 * 32 + tr;
+    const int64_t cc = c0 + cb * 32;
+    if (r < rows && cc < cols) {
+      float v[32];
+      const T* tp = tile + tr * LDT + cb * 32;
+#pragma unroll
+      for (int u = 0; u < 32 / VEC; ++u) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(tp + u * VEC);
+        float tmp[VEC];
+        Elem<T>::unpack(raw, tmp);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) v[u * VEC + j] = tmp[j];
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      const int e = mx_block_exponent(amax);
+      const float inv = mx_inv_scale(e);
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        w[k] = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[k] |= e4m3_encode(v[4 * k + t] * inv) << (8 * t);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(qr + (bz * rows + r) * cols + cc);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      scr[(bz * rows + r) * (cols / 32) + cc / 32] = static_cast<uint8_t>(e + 127);
+    }
+  }
 }
 
 }  // namespace
@@ -191,11 +230,25 @@ void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows,
   const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
                   static_cast<unsigned>(batch));
   if (src_dtype == MOE_F32)
-    MOE_LAUNCH("mx_quantize_cols", mx_cols_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(src), rows,
-               cols, seg, nseg, ldq, q, sc);
+    MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false>), grid, dim3(256), 0, s,
+               static_cast<const float*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
   else
-    MOE_LAUNCH("mx_quantize_cols", mx_cols_kernel<uint16_t>, grid, dim3(256), 0, s,
-               static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc);
+    MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false>), grid, dim3(256), 0, s,
+               static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+}
+
+void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, uint8_t* qc,
+                    uint8_t* sc, uint8_t* qr, uint8_t* scr, hipStream_t s) {
+  const int64_t nblk = rows / 32;
+  if (nblk == 0 || cols == 0 || batch == 0) return;
+  const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
+                  static_cast<unsigned>(batch));
+  if (src_dtype == MOE_F32)
+    MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<float, true>), grid, dim3(256), 0, s,
+               static_cast<const float*>(src), rows, cols, nullptr, 0, rows, qc, sc, qr, scr);
+  else
+    MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<uint16_t, true>), grid, dim3(256), 0, s,
+               static_cast<const uint16_t*>(src), rows, cols, nullptr, 0, rows, qc, sc, qr, scr);
 }
 
 }  // namespace moe

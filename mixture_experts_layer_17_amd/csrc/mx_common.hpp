@@ -57,10 +57,21 @@ void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, 
 void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
                     int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s);
 
+//  both layouts of a [batch, rows, cols] source from one read (no segments; rows % 32 == 0, cols % 32 == 0):
+//  column layout qc [batch][cols][rows], sc [batch][cols][rows/32] and row layout qr [batch][rows][cols],
+//  scr [batch][rows][cols/32].
+void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, uint8_t* qc,
+                    uint8_t* sc, uint8_t* qr, uint8_t* scr, hipStream_t s);
+
 // MXFP8 expert FFN (gemm_mx.hip).
 size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd);
 int ffn_mx_bm(int64_t R, int E);  // row-tile height for this workload
-int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, char* scratch, hipStream_t s);
-int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, char* scratch, hipStream_t s);
+//  wcache: NULL, or a weight cache built by mx_wcache_build for the same weights (then no weight is quantised)
+int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* scratch, hipStream_t s);
+int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache, char* scratch,
+               hipStream_t s);
+size_t mx_wcache_bytes(int E, int d, int f);
+void mx_wcache_build(const void* wg, const void* wu, const void* wd, int E, int d, int f, char* cache,
+                     hipStream_t s);
 
 }  // namespace moe

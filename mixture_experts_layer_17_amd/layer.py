@@ -32,9 +32,10 @@ def to_device(inp: dict, device="cuda") -> dict:
 class LayerStep:
     """Preallocated buffers and workspaces for one layer step of workload ``w``."""
 
-    def __init__(self, w: Workload, dev_inputs: dict):
+    def __init__(self, w: Workload, dev_inputs: dict, mx_weight_cache: bool = False):
         self.w = w
         self.inp = dev_inputs
+        self.mx_wcache = None
         x = dev_inputs["x"]
         dev = x.device
         T, d, E, k, f, R = w.T, w.d, w.E, w.k, w.f, w.R
@@ -72,6 +73,14 @@ class LayerStep:
         if self.linear_router:
             self.dw_router = torch.empty_like(dev_inputs["w_router"])
             self.router_ws = B._ws(B.lib().moe_router_logits_bwd_workspace(T, d, E), dev)
+        if mx_weight_cache and w.prec == "mxfp8":
+            self.build_weight_cache()
+
+    def build_weight_cache(self):
+        """Quantise the expert weights once (both orientations); later steps quantise no weight."""
+        inp = self.inp
+        self.mx_wcache = B.moe_mx_weight_cache_build(inp["w_gate"], inp["w_up"], inp["w_down"], cache=self.mx_wcache)
+        return self.mx_wcache
 
     # ------------------------------------------------------------------ steps
     def forward(self):
@@ -81,7 +90,7 @@ class LayerStep:
         B.moe_route_topk(self.logits, w.k, out=self.route, ws=self.route_ws)
         B.moe_dispatch(inp["x"], self.route["perm_dst"], w.k, out=self.x_perm)
         B.moe_grouped_ffn_fwd(self.x_perm, self.route["offsets"], inp["w_gate"], inp["w_up"], inp["w_down"], w.prec,
-                              out=self.ffn, ws=self.ffn_ws_f)
+                              out=self.ffn, ws=self.ffn_ws_f, mx_wcache=self.mx_wcache)
         B.moe_combine(self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"], out=self.out)
         return self.out
 
@@ -92,7 +101,7 @@ class LayerStep:
                           dy_perm=self.dy_perm, dgates=self.dgates)
         B.moe_grouped_ffn_bwd(self.dy_perm, self.x_perm, self.ffn["h_gate"], self.ffn["h_up"], self.ffn["a_act"],
                               self.route["offsets"], self.route["mx_blk_offsets"], inp["w_gate"], inp["w_up"],
-                              inp["w_down"], w.prec, out=self.grads, ws=self.ffn_ws_b)
+                              inp["w_down"], w.prec, out=self.grads, ws=self.ffn_ws_b, mx_wcache=self.mx_wcache)
         B.moe_dispatch_bwd(self.grads["dx_perm"], self.route["perm_dst"], w.k, out=self.dx)
         B.moe_route_topk_bwd(self.route["gates"], self.dgates, self.route["topk_idx"], w.E, out=self.dlogits)
         if self.linear_router:

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert L.moe_status_str(0) == b"ok"
     assert L.moe_status_str(3) == b"workspace too small"
 
@@ -63,16 +63,31 @@ def test_route_topk_validation(L):
 
 def test_ffn_validation(L):
     s = None
-    args = [FAKE] * 9
+    args = [FAKE] * 10
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1000, 1, *args, FAKE, 1 << 30, s) == EUNSUP   # f % 64
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 7, *args, FAKE, 1 << 30, s) == EINVAL   # bad precision
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *args, FAKE, 16, s) == EWS
-    bargs = [FAKE] * 14
+    bargs = [FAKE] * 15
     assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *bargs, FAKE, 16, s) == EWS
-    bargs_nomx = [FAKE, None] + [FAKE] * 12
+    bargs_nomx = [FAKE, None] + [FAKE] * 13
     assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 2, *bargs_nomx, FAKE, 1 << 40, s) == EINVAL
-    unaligned = [FAKE] + [ctypes.c_void_p(0x10008)] + [FAKE] * 7
+    unaligned = [FAKE] + [ctypes.c_void_p(0x10008)] + [FAKE] * 8
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *unaligned, FAKE, 1 << 30, s) == EINVAL
+    bad_cache = [FAKE] * 5 + [ctypes.c_void_p(0x10004)] + [FAKE] * 4        # unaligned weight cache
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 2, *bad_cache, FAKE, 1 << 40, s) == EINVAL
+
+
+def test_mx_weight_cache_validation(L):
+    s = None
+    E, d, f = 8, 256, 384
+    n = L.moe_mx_weight_cache_bytes(E, d, f)
+    assert n >= 6 * E * d * f * 33 // 32 and n < 6 * E * d * f * 33 // 32 + 12 * 256
+    assert L.moe_mx_weight_cache_bytes(E, d, f) == n                      # a pure function of the shape
+    assert L.moe_mx_weight_cache_bytes(0, d, f) == 0
+    assert L.moe_mx_weight_cache_build(FAKE, FAKE, FAKE, E, d, 320, FAKE, 1 << 40, s) == EUNSUP   # f % 128
+    assert L.moe_mx_weight_cache_build(FAKE, None, FAKE, E, d, f, FAKE, n, s) == EINVAL          # null weight
+    assert L.moe_mx_weight_cache_build(FAKE, FAKE, FAKE, E, d, f, FAKE, n - 1, s) == EWS         # too small
+    assert L.moe_mx_weight_cache_build(FAKE, FAKE, FAKE, 300, d, f, FAKE, 1 << 40, s) == EINVAL  # E > 256
 
 
 def test_permute_and_quantiser_validation(L):

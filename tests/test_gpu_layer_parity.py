@@ -36,6 +36,8 @@ SMALL = {
     "bf16-big-tiles-k2": wl.scaled(W[3], T=2100, d=256, f=512, E=4, k=2),
     "mxfp8-e16": wl.scaled(W[5], T=700, d=256, f=384, E=16),
     "mxfp8-e128": wl.scaled(W[5], T=1536, d=256, f=256),
+    # >= 1024 rows per expert and d, f multiples of 256: the 256 x 256 MX tiles, ragged segment ends
+    "mxfp8-big-tiles": wl.scaled(W[5], T=2300, d=512, f=256, E=2, k=1),
 }
 
 
@@ -58,6 +60,20 @@ def test_layer_deterministic(gpu):
     inp = wl.make_inputs(w)
     a, _ = gu.run_gpu_step(w, inp)
     b, _ = gu.run_gpu_step(w, inp)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["mxfp8-e16", "mxfp8-big-tiles"])
+def test_mx_weight_cache_bit_identical(gpu, name):
+    """A step on pre-quantised weights (moe_mx_weight_cache_build) gives the same bits as one that quantises
+    the weights itself."""
+    w = SMALL[name]
+    gu.say(f"case weight cache {name}")
+    inp = wl.make_inputs(w)
+    a, _ = gu.run_gpu_step(w, inp)
+    b, step = gu.run_gpu_step(w, inp, mx_weight_cache=True)
+    assert step.mx_wcache is not None
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
