@@ -114,6 +114,52 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
             "numpy": np.__version__}
 
 
+def timed_steps(step, steps: int, warmup: int) -> float:
+    """ms per layer step over `steps` steps after `warmup` untimed ones."""
+    import torch
+    for _ in range(warmup):
+        step.step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step.step()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def pool_sweep(args) -> int:
+    """Expert-pool sweep at a fixed token count: how the layer's throughput moves as the same routed rows
+    spread over more, smaller experts (the pages report a small drop from 8 to 128 experts at top-4)."""
+    import torch
+
+    from mixture_experts_layer_17_amd import binding as B
+    from mixture_experts_layer_17_amd import layer as L
+    from mixture_experts_layer_17_amd import workloads as wl
+
+    rows = []
+    for E in (8, 16, 32, 64, 128):
+        w = wl.scaled(wl.WORKLOADS[3], E=E, name=f"bf16-pool-e{E}")
+        print(f"# pool sweep E={E}: generating inputs", file=sys.stderr, flush=True)
+        step = L.LayerStep(w, L.to_device(wl.make_inputs(w, seed=args.seed)))
+        ms = timed_steps(step, args.steps, args.warmup)
+        rs = B.moe_route_stats(step.route["counts"]).cpu().tolist()
+        rows.append({"E": E, "tokens_per_s": w.T / (ms * 1e-3), "ms_per_step": ms,
+                     "gemm_tflops_est": 18.0 * w.R * w.d * w.f / (ms * 1e-3) / 1e12,
+                     "max_rows": rs[0], "min_rows": rs[1], "empty_experts": rs[2]})
+        print(f"# E={E}: {rows[-1]['tokens_per_s']:.0f} tokens/s", file=sys.stderr, flush=True)
+        del step
+        torch.cuda.empty_cache()
+    base = rows[0]["tokens_per_s"]
+    for r in rows:
+        r["vs_e8"] = r["tokens_per_s"] / base
+    print(json.dumps({"pool_sweep": rows, "config": "bf16, T=16384, d=2048, k=4, f=1024, N(0,1) router logits, "
+                      "whole-layer fwd+bwd tokens/s (gemm_tflops_est: 18 R d f over the whole step)",
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +169,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=17)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pool-sweep", action="store_true",
+                    help="only time the bf16 layer at T=16384, d=2048, k=4, f=1024 for E = 8, 16, 32, 64, 128 "
+                         "(N(0,1) router logits) and print one JSON line with the sweep")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -152,6 +201,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.pool_sweep:
+        return pool_sweep(args)
     w = wl.WORKLOADS[args.workload]
     print(f"# workload {w.name} {w.describe()}: generating inputs", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed=args.seed)
@@ -178,6 +229,7 @@ def main() -> int:
     kern = B.moe_timing_report()
     B.moe_timing_enable(False)
     peak_mem = torch.cuda.max_memory_allocated()
+    rs = B.moe_route_stats(step.route["counts"]).cpu().tolist()  # after the timed region
 
     s = 4 if w.storage == "f32" else 2
     per_step_us = {name: 1e3 * ms / args.steps for name, (n, ms) in kern.items()}
@@ -229,6 +281,8 @@ def main() -> int:
         "hbm_kernels_gbps": memk,
         "kernels_us_per_step": {k: round(v, 2) for k, v in sorted(per_step_us.items())},
         "peak_mem_gib": peak_mem / 2**30,
+        "routing_stats": {"max_rows": rs[0], "min_rows": rs[1], "empty_experts": rs[2], "rows": rs[3],
+                          "max_over_mean": rs[0] * w.E / max(rs[3], 1)},
     }
     if w.prec == "mxfp8":
         # the same step on pre-quantised weights (moe_mx_weight_cache_build): the weights are quantised once per

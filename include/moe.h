@@ -114,6 +114,14 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
 int moe_route_topk_bwd(const float* gates, const float* dgates, const int32_t* topk_idx, int64_t T,
                        int32_t E, int32_t k, float* dlogits, void* stream);
 
+/* Load statistics of a routing ("Scaling to the trillion-parameter range":
+ * a balance metric alone can be gamed, so the observable load is exported).
+ * counts [E] int32 (from moe_route_topk), 1 <= E <= 256; stats [4] int32 on
+ * the device, overwritten: {largest expert's rows, smallest expert's rows,
+ * number of experts with no rows, total rows}.  MOE_EINVAL for a bad E or a
+ * null pointer. */
+int moe_route_stats(const int32_t* counts, int32_t E, int32_t* stats, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Row-wise dispatch and weighted combine ("Scaling and optimizing MoE
  * training": routed data goes directly into the experts' input buffers).

@@ -42,6 +42,7 @@ _SIGS = {
     "moe_grouped_ffn_fwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 10 + [_c_void_p, _sz, _c_void_p]),
     "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 15 + [_c_void_p, _sz, _c_void_p]),
     "moe_mx_weight_cache_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_route_stats": (_int, [_c_void_p, _i32, _c_void_p, _c_void_p]),
     "moe_mx_weight_cache_build": (_int, [_c_void_p] * 3 + [_i32, _i32, _i32, _c_void_p, _sz, _c_void_p]),
     "mx_quantize": (_int, [_c_void_p, _int, _i64, _i64, _i64, _i32, _c_void_p, _i32, _c_void_p, _c_void_p,
                            _c_void_p]),
@@ -189,6 +190,14 @@ def moe_combine_bwd(dout, y_perm, gates, perm_dst, dy_perm=None, dgates=None):
     _check(lib().moe_combine_bwd(_p(dout), _p(y_perm), _dtype_code(dout), _p(gates), _p(perm_dst), T, d, k,
                                  _p(dy_perm), _p(dgates), _stream()), "moe_combine_bwd")
     return dy_perm, dgates
+
+
+def moe_route_stats(counts, out=None):
+    """counts [E] int32 (device) -> int32 [4] on the device: max rows, min rows, empty experts, total rows."""
+    E = counts.shape[0]
+    out = torch.empty(4, dtype=torch.int32, device=counts.device) if out is None else out
+    _check(lib().moe_route_stats(_p(counts), E, _p(out), _stream()), "moe_route_stats")
+    return out
 
 
 # --------------------------------------------------------------------------- grouped FFN

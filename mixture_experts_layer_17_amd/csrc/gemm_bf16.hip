@@ -13,9 +13,11 @@
 // read as 16-byte fragments; operands contiguous along M or N (the weights of
 // the forward GEMMs, both operands of the weight-gradient GEMMs, whose K is the
 // token axis) are read with the transposing LDS read ds_read_b64_tr_b16, two
-// per fragment.  Two tile shapes: 256 x 256 outputs per workgroup (8 waves of
-// 128 x 64) for long expert segments and the weight gradients, 128 x 128 (4
-// waves of 64 x 64) for short segments.  Epilogues go through LDS so that
+// per fragment.  Tile shapes: 256 x 256 outputs per workgroup (8 waves of
+// 128 x 64) for long expert segments and the weight gradients; for short
+// segments 128-row tiles, 128 x 256 (8 waves of 64 x 64, K step 32, two
+// workgroups per CU) for the forward GEMMs and 128 x 128 (4 waves of 64 x 64)
+// for the backward ones.  Epilogues go through LDS so that
 // global stores (and the Hg/Hu loads of the SwiGLU backward) are 16-byte vectors.
 //
 // MFMA operand layout (32x32x16 bf16): lane l supplies A[m = l % 32][k = 8(l/32) .. +7]
@@ -70,6 +72,8 @@ struct Cfg {
 #endif
 using Big = Cfg<256, 256, 2, MOE_BIG_WN, MOE_BIG_BK, MOE_BIG_NA, MOE_BIG_NB>;
 using Small = Cfg<128, 128, 2, 2, MOE_SMALL_BK, MOE_SMALL_NA, MOE_SMALL_NB>;
+// 128 x 256, 8 waves of 64 x 64, K step 32: two workgroups per CU (short segments, forward GEMMs)
+using Mid = Cfg<128, 256, 2, 4, 32, 3, 2>;
 
 // K-contiguous operand: element (mn, k) at m0[mn*ld + k] for k < ksplit, else
 // m1[mn*ld + k - ksplit]; rows mn >= mn_valid read as zero.
@@ -436,7 +440,7 @@ int launch_cfg(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s) {
 }
 
 // Row-tile height of the rows-by-expert GEMMs: 256 when the average expert
-// segment holds at least four such tiles, else 128.
+// segment holds at least four such tiles, else 128 (Small and Mid share it).
 bool big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 1024; }
 // Weight-gradient tiles: 256 x 256 when d and f fill them.
 bool big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
@@ -448,7 +452,10 @@ int ffn_bf16_bm(int64_t R, int E) { return big_rows(R, E) ? Big::BM : Small::BM;
 int launch_ffn_bf16(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s) {
   const bool wgrad = kind == kG4 || kind == kG6;
   const bool big = wgrad ? big_wgrad(a) : big_rows(a.R, a.E);
-  return big ? launch_cfg<Big>(kind, a, max_tiles, s) : launch_cfg<Small>(kind, a, max_tiles, s);
+  if (big) return launch_cfg<Big>(kind, a, max_tiles, s);
+  // short segments: 128-row tiles; the forward GEMMs do better 256 wide at two workgroups per CU
+  if (kind == kG1 || kind == kG2) return launch_cfg<Mid>(kind, a, max_tiles, s);
+  return launch_cfg<Small>(kind, a, max_tiles, s);
 }
 
 }  // namespace moe

@@ -238,10 +238,46 @@ bool route_args_ok(int64_t T, int E, int k) {
   return T >= 0 && E >= 1 && E <= kMaxE && k >= 1 && k <= kMaxK && k <= E && T * k < (1ll << 31);
 }
 
+// Load statistics of one routing from its per-expert row counts: max, min,
+// number of empty experts, total rows (one workgroup, E <= 256).
+__global__ __launch_bounds__(256) void route_stats_kernel(const int32_t* __restrict__ counts, int E,
+                                                          int32_t* __restrict__ stats) {
+  __shared__ int32_t mx[256], mn[256], em[256], sm[256];
+  const int t = threadIdx.x;
+  const int32_t c = t < E ? counts[t] : 0;
+  mx[t] = t < E ? c : INT32_MIN;
+  mn[t] = t < E ? c : INT32_MAX;
+  em[t] = (t < E && c == 0) ? 1 : 0;
+  sm[t] = c;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) {
+      mx[t] = mx[t] > mx[t + o] ? mx[t] : mx[t + o];
+      mn[t] = mn[t] < mn[t + o] ? mn[t] : mn[t + o];
+      em[t] += em[t + o];
+      sm[t] += sm[t + o];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    stats[0] = mx[0];
+    stats[1] = mn[0];
+    stats[2] = em[0];
+    stats[3] = sm[0];
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" int moe_route_stats(const int32_t* counts, int32_t E, int32_t* stats, void* stream) {
+  if (E < 1 || E > kMaxE || !counts || !stats) return MOE_EINVAL;
+  MOE_LAUNCH("route_stats", route_stats_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), counts, E,
+             stats);
+  return launch_status();
+}
 
 extern "C" size_t moe_route_topk_workspace(int64_t T, int32_t E, int32_t k) {
   if (!route_args_ok(T, E, k)) return 0;

@@ -142,6 +142,15 @@ def routing_metadata(topk_idx, num_experts):
 # ----------------------------------------------------------------------------
 
 
+def routing_stats(counts):
+    """Load statistics of one routing (Olmo-core 3 announcement, "Scaling to the
+    trillion-parameter range": a balance metric can be gamed, so the observable
+    per-expert load is what gets reported): [largest expert's rows, smallest
+    expert's rows, number of experts with no rows, total rows]."""
+    c = np.asarray(counts, np.int64)
+    return np.array([c.max(), c.min(), int(np.sum(c == 0)), c.sum()], np.int64)
+
+
 def dispatch(x, perm_src, k):
     """Row-wise dispatch: x_perm[r] = x[perm_src[r] // k] (an exact copy).
 

@@ -77,6 +77,14 @@ def test_ffn_validation(L):
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 2, *bad_cache, FAKE, 1 << 40, s) == EINVAL
 
 
+def test_route_stats_validation(L):
+    s = None
+    assert L.moe_route_stats(FAKE, 0, FAKE, s) == EINVAL
+    assert L.moe_route_stats(FAKE, 257, FAKE, s) == EINVAL
+    assert L.moe_route_stats(None, 8, FAKE, s) == EINVAL
+    assert L.moe_route_stats(FAKE, 8, None, s) == EINVAL
+
+
 def test_mx_weight_cache_validation(L):
     s = None
     E, d, f = 8, 256, 384

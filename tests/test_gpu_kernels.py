@@ -48,6 +48,20 @@ def test_route_topk_bit_exact(gpu, T, E, k, kind):
     assert gu.rel_err(out["gates"].cpu().numpy(), mo.topk_gates(lg, idx)) <= 1e-5
 
 
+@pytest.mark.parametrize("T,E,k,bias", [(1000, 8, 4, 0.0), (2048, 128, 4, 3.0), (333, 256, 8, 3.0), (50, 1, 1, 0.0)])
+def test_route_stats_bit_exact(gpu, T, E, k, bias):
+    """Load statistics from the device routing equal the oracle's from its own routing (uniform and
+    zipf-biased logits, the latter with empty experts)."""
+    r = np.random.default_rng(T + E)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    lg += (bias * np.log(1.0 / (r.permutation(E) + 1))).astype(np.float32)
+    out = B.moe_route_topk(torch.from_numpy(lg).cuda(), k)
+    st = B.moe_route_stats(out["counts"])
+    torch.cuda.synchronize()
+    ref = mo.routing_stats(mo.routing_metadata(mo.topk_select(lg, k), E)["counts"])
+    np.testing.assert_array_equal(st.cpu().numpy(), ref)
+
+
 def test_route_topk_empty_batch(gpu):
     lg = torch.empty((0, 16), dtype=torch.float32, device="cuda")
     out = B.moe_route_topk(lg, 4)

@@ -209,6 +209,19 @@ def check_forward(layer_fn):
         assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
 
 
+def test_routing_stats_hand_example_and_special_cases():
+    # four tokens, top-2 of five experts, counted by hand: expert 0 gets 4 rows, 1 gets 2, 2 and 3 one
+    # each, 4 none
+    idx = np.array([[0, 1], [0, 2], [0, 1], [3, 0]])
+    counts = mo.routing_metadata(idx, 5)["counts"]
+    assert counts.tolist() == [4, 2, 1, 1, 0]
+    assert mo.routing_stats(counts).tolist() == [4, 0, 1, 8]
+    # one expert takes every row; k = E spreads every token over all experts
+    assert mo.routing_stats([12]).tolist() == [12, 12, 0, 12]
+    full = mo.routing_metadata(np.tile(np.arange(6), (7, 1)), 6)["counts"]
+    assert mo.routing_stats(full).tolist() == [7, 7, 0, 42]
+
+
 def test_forward_matches_dense_bruteforce():
     check_forward(oracle_out)
 
