@@ -82,9 +82,21 @@ int tile_bm(int prec, int64_t R, int E) {
 
 size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }
 
-// Workspace layout: [tile table][dHg][dHu] (backward only) [MX scratch] (MXFP8 only).
+// Workspace layout: [tile table][G3 tile table (bf16 backward, see below)][dHg][dHu] (backward only)
+// [MX scratch] (MXFP8 only).
+// bf16 backward: the SwiGLU-backward GEMM (G3) walks 128-row tiles of its own
+// when the others use 256-row ones (its epilogue then overlaps the other
+// workgroup's main loop on the same CU).
+bool g3_own_table(const FfnShape& s) { return s.prec == MOE_BF16 && tile_bm(s.prec, s.R, s.E) != 128; }
+
+size_t one_table_bytes(int64_t R, int E, int bm) {
+  return align_up(static_cast<size_t>(max_m_tiles(R, E, bm) + 1) * sizeof(int4), 256);
+}
+
 size_t tiles_bytes(const FfnShape& s) {
-  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec, s.R, s.E)) + 1) * sizeof(int4), 256);
+  size_t b = one_table_bytes(s.R, s.E, tile_bm(s.prec, s.R, s.E));
+  if (g3_own_table(s)) b += one_table_bytes(s.R, s.E, 128);
+  return b;
 }
 
 size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {
@@ -164,6 +176,7 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.offsets = offsets;
   a.tiles = tiles;
   a.max_tiles = mt;
+  a.bm = bm;
   a.E = E; a.d = d; a.f = f; a.R = R;
   a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
   a.o_hg = h_gate; a.o_hu = h_up; a.o_act = a_act; a.act = a_act; a.o_y = y_perm;
@@ -207,6 +220,7 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.offsets = offsets;
   a.tiles = tiles;
   a.max_tiles = mt;
+  a.bm = bm;
   a.E = E; a.d = d; a.f = f; a.R = R;
   a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
   a.hg = h_gate; a.hu = h_up; a.act = a_act; a.dy = dy_perm;
@@ -219,7 +233,17 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
   int st = MOE_OK;
   if (R > 0) {
-    st = launch(kG3, a, mt, s);
+    if (g3_own_table(sh)) {
+      FfnArgs a3 = a;
+      a3.bm = 128;
+      a3.max_tiles = max_m_tiles(R, E, 128);
+      int4* t3 = reinterpret_cast<int4*>(wsb + one_table_bytes(R, E, bm));
+      a3.tiles = t3;
+      launch_tile_map(offsets, E, 128, R, a3.max_tiles, t3, s);
+      st = launch(kG3, a3, a3.max_tiles, s);
+    } else {
+      st = launch(kG3, a, mt, s);
+    }
     if (st == MOE_OK) st = launch(kG5, a, mt, s);
   }
   if (st == MOE_OK) st = launch(kG4, a, mt, s);

@@ -26,6 +26,7 @@ struct FfnArgs {
   const int4* tiles;       // M-tile table: {expert, row0, rows, 0}; expert < 0 past the end;
                            // entry [max_tiles] = {number of live tiles, 0, 0, 0}
   int64_t max_tiles;
+  int bm;                  // row-tile height the tile table was built for
   int E, d, f;
   int64_t R;
   // inputs

@@ -14,10 +14,11 @@
 // the forward GEMMs, both operands of the weight-gradient GEMMs, whose K is the
 // token axis) are read with the transposing LDS read ds_read_b64_tr_b16, two
 // per fragment.  Tile shapes: 256 x 256 outputs per workgroup (8 waves of
-// 128 x 64) for long expert segments and the weight gradients; for short
-// segments 128-row tiles, 128 x 256 (8 waves of 64 x 64, K step 32, two
-// workgroups per CU) for the forward GEMMs and 128 x 128 (4 waves of 64 x 64)
-// for the backward ones.  Epilogues go through LDS so that
+// 128 x 64) for long expert segments (except the SwiGLU-backward GEMM) and the
+// weight gradients; otherwise 128-row tiles: 128 x 256 (8 waves of 64 x 64, K
+// step 32, two workgroups per CU) for the forward GEMMs and 128 x 128 (4 waves
+// of 64 x 64, two workgroups per CU, so that one's epilogue overlaps the
+// other's main loop) for the backward ones.  Epilogues go through LDS so that
 // global stores (and the Hg/Hu loads of the SwiGLU backward) are 16-byte vectors.
 //
 // MFMA operand layout (32x32x16 bf16): lane l supplies A[m = l % 32][k = 8(l/32) .. +7]
@@ -451,7 +452,7 @@ int ffn_bf16_bm(int64_t R, int E) { return big_rows(R, E) ? Big::BM : Small::BM;
 
 int launch_ffn_bf16(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s) {
   const bool wgrad = kind == kG4 || kind == kG6;
-  const bool big = wgrad ? big_wgrad(a) : big_rows(a.R, a.E);
+  const bool big = wgrad ? big_wgrad(a) : a.bm == Big::BM;
   if (big) return launch_cfg<Big>(kind, a, max_tiles, s);
   // short segments: 128-row tiles; the forward GEMMs do better 256 wide at two workgroups per CU
   if (kind == kG1 || kind == kG2) return launch_cfg<Mid>(kind, a, max_tiles, s);

@@ -346,7 +346,7 @@ bool mx_big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
 
 int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
   const bool wgrad = kind == kG4 || kind == kG6;
-  const bool big = wgrad ? mx_big_wgrad(a.f) : mx_big_rows(a.f.R, a.f.E);
+  const bool big = wgrad ? mx_big_wgrad(a.f) : a.f.bm == MxBig::BM;
   return big ? launch_mx_cfg<MxBig>(kind, a, max_tiles, s) : launch_mx_cfg<MxSmall>(kind, a, max_tiles, s);
 }
 
