@@ -43,21 +43,25 @@ struct MxCfg {
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int BK = 128;
   static constexpr int kA = BM * BK, kB = BN * BK;  // bytes per stage
-  static constexpr int kScales = 2 * (BM + BN) * 4;   // two stages of one scale word per tile row
+  // scale words: per stage, two groups (the K-step's four blocks may straddle two) x [A: 1 KB, B: 2 x 1 KB]
+  static constexpr int kScaleStage = 2 * 3 * 1024;
+  static constexpr int kScales = 2 * kScaleStage;
+  static_assert(BM <= 256 && BN <= 256, "one 1 KB scale run per operand (half) and group");
   static constexpr int kEpi = cmax(2 * BM * (BN / 2 + 8), BM * (BN + 8));  // bf16 elements
   static constexpr int kLds = cmax((2 * kA + 2 * kB + kScales) / 2, kEpi);  // bf16 elements
   static_assert(kLds * 2 <= 160 * 1024, "LDS budget");
-  static_assert(BM + BN == kThreads, "one thread per tile row fetches the scales");
 };
 using MxBig = MxCfg<256, 256, 2, 4>;
 using MxSmall = MxCfg<128, 128, 2, 2>;
 
 // K-contiguous fp8 operand with block scales: element (mn, k) at
-// q[mn*ld + k_base + k], its scale at s[mn*(ld/32) + (k_base + k)/32]; k >=
-// ksplit reads the second matrix at k - ksplit.  Dual operands (template flag)
-// take tile rows [0, W/2) from the first matrix and [W/2, W) from the second.
-// Rows mn >= mn_valid (of each matrix) read as zero; K elements past k_valid
-// get zero-weight scales.
+// q[mn*ld + k_base + k]; k >= ksplit reads the second matrix at k - ksplit.
+// Dual operands (template flag) take tile rows [0, W/2) from the first matrix
+// and [W/2, W) from the second.  Scales are in the grouped layout: the word of
+// tile row mn for block group G (blocks 4G .. 4G+3 of the row) is at
+// s + G*gs + 4*mn (s already offset to the tile's first row, gs = 4 x rows of
+// the scale matrix).  Rows mn >= mn_valid (of each matrix) read as zero; K
+// elements past k_valid get zero-weight scales.
 struct MxKc {
   const uint8_t* q0;
   const uint8_t* q1;
@@ -68,6 +72,7 @@ struct MxKc {
   int k_valid;     // K elements of this problem (multiple of 32)
   int ksplit;
   int mn_valid;
+  int64_t gs;      // bytes between scale groups
 };
 
 // LDS-DMA loads of a ROWS x 128-byte tile (K-step at k0).
@@ -95,33 +100,12 @@ __device__ __forceinline__ void mx_dma(const MxKc& op, int k0, uint8_t* dst, int
   }
 }
 
-// The four scale bytes (blocks 0..3 of the K-step at k0) of tile row `row`,
-// byte j = block j; 0 (2^-127) past the valid rows or K range.  One dword load
-// when the row's scales for the step are 4-byte aligned, else four byte loads.
-template <bool DUAL, int ROWS>
-__device__ __forceinline__ uint32_t mx_scale_word(const MxKc& op, int row, int k0) {
-  const uint8_t* s = op.s0;
-  int r = row;
-  int kk = k0;
-  if constexpr (DUAL) {
-    if (row >= ROWS / 2) {
-      s = op.s1;
-      r = row - ROWS / 2;
-    }
-  } else if (k0 >= op.ksplit) {
-    s = op.s1;
-    kk = k0 - op.ksplit;
-  }
-  if (r >= op.mn_valid) return 0u;
-  const int64_t sld = op.ld / 32;
-  const uint8_t* p = s + r * sld + (op.k_base + kk) / 32;
-  const int nb = (op.k_valid - k0) / 32;  // valid blocks in this step (may exceed 4)
-  if (nb >= 4 && ((reinterpret_cast<uintptr_t>(p) & 3) == 0)) return *reinterpret_cast<const uint32_t*>(p);
-  uint32_t w = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (j < nb) w |= static_cast<uint32_t>(p[j]) << (8 * j);
-  return w;
+// LDS-DMA of one scale run: the words of `rows` tile rows for block group G
+// (zeros past rows_valid and for lanes past the run).
+__device__ __forceinline__ void scale_dma(const uint8_t* s, int64_t gs, int64_t G, int rows_valid, uint8_t* dst,
+                                          int lane) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(s + G * gs, static_cast<int64_t>(rows_valid) * 4);
+  dma16(r, dst, lane * 16);
 }
 
 // One fp8 MFMA operand (32 bytes) from a 128-byte-row tile: row `row`, K-slice ks.
@@ -147,9 +131,9 @@ __device__ __forceinline__ int b_row(int wn, int j) {
 }
 
 // C = A B^T over K = [0, K), both operands K-contiguous fp8 with block scales.
-// Thread t fetches the scale word of tile row t (A rows, then B rows) for the
-// next K-step while the current one is consumed, and parks it in the LDS slot
-// of that step; the lanes read their own rows' words from there.
+// Each K-step's scale words (groups G and, when the step starts mid-group,
+// G+1) come in by LDS-DMA with the data; a lane shifts its row's four bytes
+// out of the two words.
 template <class C, bool BDUAL>
 __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, int K, uint8_t* lds, int tid,
                                             Acc<C>& acc) {
@@ -166,37 +150,67 @@ __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, in
   if (nk == 0) return;
   uint8_t* qa = lds;                                          // A stages
   uint8_t* qb = lds + 2 * C::kA;                              // B stages
-  uint32_t* sw = reinterpret_cast<uint32_t*>(lds + 2 * C::kA + 2 * C::kB);  // [2][BM + BN] scale words
+  uint8_t* sl = lds + 2 * C::kA + 2 * C::kB;                  // [2 stages][2 groups][A 1 KB | B 2 KB]
+  // the problem's K offset in blocks decides how K-steps sit in the groups (the same for A and B)
+  const int o = static_cast<int>((aop.k_base / 32) & 3);
+  const int arows = aop.mn_valid < C::BM ? aop.mn_valid : C::BM;
+  constexpr int BH = BDUAL ? C::BN / 2 : C::BN;
+  const int brows = bop.mn_valid < BH ? bop.mn_valid : BH;
   auto issue = [&](int kt) {
-    mx_dma<C, C::BM, false>(aop, kt * C::BK, qa + (kt & 1) * C::kA, wave, lane);
-    mx_dma<C, C::BN, BDUAL>(bop, kt * C::BK, qb + (kt & 1) * C::kB, wave, lane);
+    const int k0 = kt * C::BK;
+    mx_dma<C, C::BM, false>(aop, k0, qa + (kt & 1) * C::kA, wave, lane);
+    mx_dma<C, C::BN, BDUAL>(bop, k0, qb + (kt & 1) * C::kB, wave, lane);
+    // scale runs: slot = group (0, 1) x {A, B half 0, B half 1}
+    const bool hi = !BDUAL && k0 >= aop.ksplit;
+    const int kk = hi ? k0 - aop.ksplit : k0;
+    const int64_t G = (aop.k_base / 32 + kk / 32) >> 2;
+    uint8_t* st = sl + (kt & 1) * C::kScaleStage;
+#pragma unroll
+    for (int slot = 0; slot < 6; ++slot) {
+      const int grp = slot / 3, part = slot % 3;
+      if (grp == 1 && o == 0) continue;
+      if (part == 2 && !BDUAL) continue;
+      if (wave != slot % C::kWaves) continue;
+      uint8_t* dst = st + grp * 3072 + part * 1024;
+      if (part == 0)
+        scale_dma(hi ? aop.s1 : aop.s0, aop.gs, G + grp, arows, dst, lane);
+      else
+        scale_dma((part == 2 || (!BDUAL && hi)) ? bop.s1 : bop.s0, bop.gs, G + grp, brows, dst, lane);
+    }
   };
-  auto fetch = [&](int kt) -> uint32_t {
-    return tid < C::BM ? mx_scale_word<false, C::BM>(aop, tid, kt * C::BK)
-                       : mx_scale_word<BDUAL, C::BN>(bop, tid - C::BM, kt * C::BK);
+  // bytes of this step's 4 blocks that lie inside the problem's K range
+  auto kmask = [&](int kt) -> uint32_t {
+    const int nb = (aop.k_valid - kt * C::BK) / 32;
+    return nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
+  };
+  // a row's four scale bytes from the staged words
+  auto word = [&](const uint8_t* st, int part, int row) -> uint32_t {
+    const uint32_t w0 = reinterpret_cast<const uint32_t*>(st + part * 1024)[row];
+    if (o == 0) return w0;
+    const uint32_t w1 = reinterpret_cast<const uint32_t*>(st + 3072 + part * 1024)[row];
+    return (w0 >> (8 * o)) | (w1 << (32 - 8 * o));
   };
   issue(0);
-  sw[tid] = fetch(0);
   for (int kt = 0; kt < nk; ++kt) {
     wait_vm<0>();
     __syncthreads();
-    uint32_t next = 0;
-    if (kt + 1 < nk) {
-      issue(kt + 1);
-      next = fetch(kt + 1);
-    }
+    if (kt + 1 < nk) issue(kt + 1);
     const uint8_t* as = qa + (kt & 1) * C::kA;
     const uint8_t* bs = qb + (kt & 1) * C::kB;
-    const uint32_t* ss = sw + (kt & 1) * (C::BM + C::BN);
+    const uint8_t* ss = sl + (kt & 1) * C::kScaleStage;
+    const uint32_t m = kmask(kt);
+    uint32_t ca[C::TM], cb[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) ca[i] = word(ss, 0, wm * C::WTM + i * 32 + (lane & 31)) & m;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int r = b_row<C, BDUAL>(wn, j) + (lane & 31);
+      cb[j] = (BDUAL && r >= C::BN / 2 ? word(ss, 2, r - C::BN / 2) : word(ss, 1, r)) & m;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // lane (g, m): scale of block 2 ks + g of its row (byte 2 ks + g of the row's word)
       const int sh = 8 * (2 * ks + g);
-      uint32_t ca[C::TM], cb[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) ca[i] = ss[wm * C::WTM + i * 32 + (lane & 31)];
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) cb[j] = ss[C::BM + b_row<C, BDUAL>(wn, j) + (lane & 31)];
       i32x8 a[C::TM], b[C::TN];
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) a[i] = mx_frag(as, wm * C::WTM + i * 32 + (lane & 31), ks, g);
@@ -210,7 +224,6 @@ __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, in
               a[i], b[j], acc[i][j], 0, 0, 0, static_cast<int>((ca[i] >> sh) & 0xFFu), 0,
               static_cast<int>((cb[j] >> sh) & 0xFFu));
     }
-    if (kt + 1 < nk) sw[((kt + 1) & 1) * (C::BM + C::BN) + tid] = next;
   }
   __syncthreads();  // the epilogue reuses the LDS
 }
@@ -247,31 +260,39 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
     const int nt = static_cast<int>(lid % gx);
     if constexpr (KIND == kG1) {
       const int n0 = nt * (C::BN / 2);
-      const MxKc a{m.xq + row0 * d, nullptr, m.xs + row0 * (d / 32), nullptr, d, 0, d, kNoSplit, rows};
+      const int64_t R = p.R;
+      const MxKc a{m.xq + row0 * d, nullptr, m.xs + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, R * 4};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * d;  // transposed Wg, Wu: [E][f][d]
-      const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + wo / 32, m.wus + wo / 32, d, 0, d, kNoSplit, f - n0};
+      const int64_t so = e * wsz / 32 + static_cast<int64_t>(n0) * 4;  // scales grouped per expert over f rows
+      const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, d, 0, d, kNoSplit, f - n0,
+                   static_cast<int64_t>(f) * 4};
       mx_mainloop<C, true>(a, b, d, lds8, tid, acc);
       epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else if constexpr (KIND == kG2) {
       const int n0 = nt * C::BN;  // over d
-      const MxKc a{m.aq + row0 * f, nullptr, m.as + row0 * (f / 32), nullptr, f, 0, f, kNoSplit, rows};
+      const MxKc a{m.aq + row0 * f, nullptr, m.as + row0 * 4, nullptr, f, 0, f, kNoSplit, rows, p.R * 4};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * f;  // transposed Wd: [E][d][f]
-      const MxKc b{m.wdq + wo, nullptr, m.wds + wo / 32, nullptr, f, 0, f, kNoSplit, d - n0};
+      const int64_t so = e * wsz / 32 + static_cast<int64_t>(n0) * 4;  // scales grouped per expert over d rows
+      const MxKc b{m.wdq + wo, nullptr, m.wds + so, nullptr, f, 0, f, kNoSplit, d - n0, static_cast<int64_t>(d) * 4};
       mx_mainloop<C, false>(a, b, f, lds8, tid, acc);
       epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
       const int n0 = nt * C::BN;  // over f
-      const MxKc a{m.dyq + row0 * d, nullptr, m.dys + row0 * (d / 32), nullptr, d, 0, d, kNoSplit, rows};
+      const MxKc a{m.dyq + row0 * d, nullptr, m.dys + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, p.R * 4};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * d;  // natural Wd: [E][f][d]
-      const MxKc b{m.wdq + wo, nullptr, m.wds + wo / 32, nullptr, d, 0, d, kNoSplit, f - n0};
+      const int64_t so = (static_cast<int64_t>(e) * f + n0) * 4;  // scales grouped over all E*f rows
+      const MxKc b{m.wdq + wo, nullptr, m.wds + so, nullptr, d, 0, d, kNoSplit, f - n0,
+                   static_cast<int64_t>(p.E) * f * 4};
       mx_mainloop<C, false>(a, b, d, lds8, tid, acc);
       epi_swiglu_bwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else {  // kG5
       const int n0 = nt * C::BN;  // over d
-      const MxKc a{m.dhgq + row0 * f, m.dhuq + row0 * f, m.dhgs + row0 * (f / 32), m.dhus + row0 * (f / 32),
-                   f, 0, 2 * f, f, rows};
+      const MxKc a{m.dhgq + row0 * f, m.dhuq + row0 * f, m.dhgs + row0 * 4, m.dhus + row0 * 4,
+                   f, 0, 2 * f, f, rows, p.R * 4};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * f;  // natural Wg, Wu: [E][d][f]
-      const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + wo / 32, m.wus + wo / 32, f, 0, 2 * f, f, d - n0};
+      const int64_t so = (static_cast<int64_t>(e) * d + n0) * 4;  // scales grouped over all E*d rows
+      const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, f, 0, 2 * f, f, d - n0,
+                   static_cast<int64_t>(p.E) * d * 4};
       mx_mainloop<C, false>(a, b, 2 * f, lds8, tid, acc);
       epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
     }
@@ -289,10 +310,10 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
     MxKc a, b;
     if constexpr (KIND == kG4) {  // dWd_e [f, d] = A_e^T dY_e
       n0 = ntile * C::BN;
-      a = MxKc{m.atq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.ats + static_cast<int64_t>(m0) * (m.ldt / 32),
-               nullptr, m.ldt, kb, K, kNoSplit, f - m0};
-      b = MxKc{m.dytq + static_cast<int64_t>(n0) * m.ldt, nullptr, m.dyts + static_cast<int64_t>(n0) * (m.ldt / 32),
-               nullptr, m.ldt, kb, K, kNoSplit, d - n0};
+      a = MxKc{m.atq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.ats + static_cast<int64_t>(m0) * 4, nullptr,
+               m.ldt, kb, K, kNoSplit, f - m0, static_cast<int64_t>(f) * 4};
+      b = MxKc{m.dytq + static_cast<int64_t>(n0) * m.ldt, nullptr, m.dyts + static_cast<int64_t>(n0) * 4, nullptr,
+               m.ldt, kb, K, kNoSplit, d - n0, static_cast<int64_t>(d) * 4};
       Cp = static_cast<uint16_t*>(p.o_dwd) + e * wsz;
       ldc = d;
       mvalid = f;
@@ -301,12 +322,12 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
       const int per = (f + C::BN - 1) / C::BN;
       const int which = ntile / per;
       n0 = (ntile % per) * C::BN;
-      a = MxKc{m.xtq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.xts + static_cast<int64_t>(m0) * (m.ldt / 32),
-               nullptr, m.ldt, kb, K, kNoSplit, d - m0};
+      a = MxKc{m.xtq + static_cast<int64_t>(m0) * m.ldt, nullptr, m.xts + static_cast<int64_t>(m0) * 4, nullptr,
+               m.ldt, kb, K, kNoSplit, d - m0, static_cast<int64_t>(d) * 4};
       const uint8_t* bq = which ? m.dhutq : m.dhgtq;
       const uint8_t* bs = which ? m.dhuts : m.dhgts;
-      b = MxKc{bq + static_cast<int64_t>(n0) * m.ldt, nullptr, bs + static_cast<int64_t>(n0) * (m.ldt / 32), nullptr,
-               m.ldt, kb, K, kNoSplit, f - n0};
+      b = MxKc{bq + static_cast<int64_t>(n0) * m.ldt, nullptr, bs + static_cast<int64_t>(n0) * 4, nullptr, m.ldt, kb,
+               K, kNoSplit, f - n0, static_cast<int64_t>(f) * 4};
       Cp = static_cast<uint16_t*>(which ? p.o_dwu : p.o_dwg) + e * wsz;
       ldc = f;
       mvalid = d;
@@ -373,7 +394,10 @@ QPair take_q(Carve& c, int64_t elems) {
   return r;
 }
 
-int64_t token_pad(int64_t R, int E) { return 32 * (cdiv(R, 32) + E); }
+// token-axis length: every expert segment padded to 32 tokens, the total to a
+// whole number of scale groups (128 tokens) plus one zero group, so that a
+// K-step starting mid-group never reads a group past the end
+int64_t token_pad(int64_t R, int E) { return 128 * (cdiv(cdiv(R, 32) + E, 4) + 1); }
 
 // Lay out (or size, when base is null) the forward and backward scratch areas.
 struct FwdBufs {
@@ -469,21 +493,21 @@ int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* sc
   MxArgs m{};
   m.f = a;
   // X along d (rows); Wg, Wu [E][d][f] along d -> [E][f][d]; Wd [E][f][d] along f -> [E][d][f]
-  launch_mx_rows(a.x, bf, a.R, a.d, b.x.q, b.x.s, s);
+  launch_mx_rows(a.x, bf, a.R, a.d, b.x.q, b.x.s, s, true);
   if (wcache) {
     Carve cc{const_cast<char*>(wcache)};
     const WCache w = carve_wcache(cc, a.E, a.d, a.f);
     m.wgq = w.wg_f.q; m.wgs = w.wg_f.s; m.wuq = w.wu_f.q; m.wus = w.wu_f.s; m.wdq = w.wd_f.q; m.wds = w.wd_f.s;
   } else {
-    launch_mx_cols(a.wg, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wg.q, b.wg.s, s);
-    launch_mx_cols(a.wu, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wu.q, b.wu.s, s);
-    launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s);
+    launch_mx_cols(a.wg, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wg.q, b.wg.s, s, true);
+    launch_mx_cols(a.wu, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wu.q, b.wu.s, s, true);
+    launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s, true);
     m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s; m.wdq = b.wd.q; m.wds = b.wd.s;
   }
   m.xq = b.x.q; m.xs = b.x.s;
   int st = launch_mx_kind(kG1, m, max_tiles, s);
   if (st != MOE_OK) return st;
-  launch_mx_rows(a.o_act, bf, a.R, a.f, b.a.q, b.a.s, s);
+  launch_mx_rows(a.o_act, bf, a.R, a.f, b.a.q, b.a.s, s, true);
   m.aq = b.a.q; m.as = b.a.s;
   return launch_mx_kind(kG2, m, max_tiles, s);
 }
@@ -506,31 +530,31 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
       const WCache w = carve_wcache(cc, a.E, a.d, a.f);
       m.wdq = w.wd_b.q; m.wds = w.wd_b.s; m.wgq = w.wg_b.q; m.wgs = w.wg_b.s; m.wuq = w.wu_b.q; m.wus = w.wu_b.s;
     } else {
-      launch_mx_rows(a.wd, bf, static_cast<int64_t>(a.E) * a.f, a.d, b.wd.q, b.wd.s, s);
+      launch_mx_rows(a.wd, bf, static_cast<int64_t>(a.E) * a.f, a.d, b.wd.q, b.wd.s, s, true);
       m.wdq = b.wd.q; m.wds = b.wd.s;
     }
     // G3: dA = dY Wd^T: dY along d, Wd natural [E][f][d] along d
-    launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s);
+    launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s, true);
     m.dyq = b.dy.q; m.dys = b.dy.s;
     st = launch_mx_kind(kG3, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f
-    launch_mx_rows(a.dhg, bf, a.R, a.f, b.dhg.q, b.dhg.s, s);
-    launch_mx_rows(a.dhu, bf, a.R, a.f, b.dhu.q, b.dhu.s, s);
+    launch_mx_rows(a.dhg, bf, a.R, a.f, b.dhg.q, b.dhg.s, s, true);
+    launch_mx_rows(a.dhu, bf, a.R, a.f, b.dhu.q, b.dhu.s, s, true);
     if (!wcache) {
-      launch_mx_rows(a.wg, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wg.q, b.wg.s, s);
-      launch_mx_rows(a.wu, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wu.q, b.wu.s, s);
+      launch_mx_rows(a.wg, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wg.q, b.wg.s, s, true);
+      launch_mx_rows(a.wu, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wu.q, b.wu.s, s, true);
       m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s;
     }
     m.dhgq = b.dhg.q; m.dhgs = b.dhg.s; m.dhuq = b.dhu.q; m.dhus = b.dhu.s;
     st = launch_mx_kind(kG5, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // weight gradients: every operand along tokens, per expert segment, transposed
-    launch_mx_cols(a.act, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.at.q, b.at.s, s);
-    launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s);
-    launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s);
-    launch_mx_cols(a.dhg, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhgt.q, b.dhgt.s, s);
-    launch_mx_cols(a.dhu, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhut.q, b.dhut.s, s);
+    launch_mx_cols(a.act, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.at.q, b.at.s, s, true);
+    launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s, true);
+    launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s, true);
+    launch_mx_cols(a.dhg, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhgt.q, b.dhgt.s, s, true);
+    launch_mx_cols(a.dhu, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhut.q, b.dhut.s, s, true);
   }
   m.atq = b.at.q; m.ats = b.at.s; m.dytq = b.dyt.q; m.dyts = b.dyt.s;
   m.xtq = b.xt.q; m.xts = b.xt.s;

@@ -30,6 +30,14 @@ __device__ __forceinline__ void load8<float>(const float* p, float* o) {
   Elem<float>::unpack(reinterpret_cast<const uint4*>(p)[1], o + 4);
 }
 
+// Scale byte of (row r, block b) of a [nrows, nblk] scale matrix: row-major
+// (the public layout) or, for the GEMM operands, grouped by four blocks (one
+// K-step of the MX GEMMs): byte ((b/4) nrows + r) 4 + b%4, so that a tile's
+// scale words for one K-step are contiguous.
+__device__ __forceinline__ int64_t scale_index(bool grouped, int64_t r, int64_t b, int64_t nrows, int64_t nblk) {
+  return grouped ? ((b >> 2) * nrows + r) * 4 + (b & 3) : r * nblk + b;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const T* __restrict__ src, int64_t nvec8,
                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
@@ -60,6 +68,46 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const T* __restrict__ src,
   if ((i & 3) == 0) sc[i >> 2] = static_cast<uint8_t>(e + 127);
 }
 
+// Row layout with grouped scales: the same streaming order as mx_rows_kernel
+// (vector i = elements [8i, 8i+8) of the flattened matrix); the 16 lanes of a
+// group (128 elements, four blocks of one row) combine their scale bytes into
+// the group's word, written at (G*nrows + r) for group G of row r.
+template <typename T>
+__global__ __launch_bounds__(256) void mx_rows_grouped_kernel(const T* __restrict__ src, uint32_t nvec8,
+                                                             uint32_t nrows, uint32_t ngpr,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool ok = i < nvec8;
+  float v[8];
+  if (ok) {
+    load8<T>(src + static_cast<int64_t>(i) * 8, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int e = mx_block_exponent(amax);
+  const float inv = mx_inv_scale(e);
+  uint32_t sw = static_cast<uint32_t>(e + 127) << (8 * ((i >> 2) & 3));
+  sw |= __shfl_xor(sw, 4, 64);
+  sw |= __shfl_xor(sw, 8, 64);
+  if (!ok) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lo |= e4m3_encode(v[j] * inv) << (8 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hi |= e4m3_encode(v[4 + j] * inv) << (8 * j);
+  reinterpret_cast<uint2*>(q)[i] = make_uint2(lo, hi);
+  if ((i & 15) == 0) {
+    const uint32_t gg = i >> 4, r = gg / ngpr, G = gg - r * ngpr;
+    reinterpret_cast<uint32_t*>(sc)[G * nrows + r] = sw;
+  }
+}
+
 // Column layout: a workgroup takes 4 consecutive 32-row blocks (in block
 // order; with segments each block has its own first row and valid rows) x 64
 // columns.  Rows come in as 16-byte vectors into LDS; wave w quantises block w
@@ -71,7 +119,7 @@ constexpr int kColW = 64;
 // thread t encodes 32 consecutive elements of tile row t/2 into the row layout
 // qr [batch, rows, cols], scr [batch, rows, cols/32] (one read of the source
 // serves both orientations).
-template <typename T, bool BOTH>
+template <typename T, bool BOTH, bool GROUPED>
 __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
                                                      const int32_t* __restrict__ seg, int nseg, int64_t ldq,
                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
@@ -169,7 +217,13 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     }
   }
   uint8_t* sb = sc + bz * cols * (ldq / 32);
-  {
+  if constexpr (GROUPED) {
+    // the four blocks of this workgroup are one group: 64 consecutive scale words
+    if (tid < kColW && c0 + tid < cols) {
+      const uint32_t w = osc[tid][0] | (osc[tid][1] << 8) | (osc[tid][2] << 16) | (static_cast<uint32_t>(osc[tid][3]) << 24);
+      reinterpret_cast<uint32_t*>(sb)[(b0 >> 2) * cols + c0 + tid] = w;
+    }
+  } else {
     const int oc = tid >> 2, j = tid & 3;
     if (c0 + oc < cols && b0 + j < nblk) sb[(c0 + oc) * (ldq / 32) + b0 + j] = osc[oc][j];
   }
@@ -204,7 +258,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
       uint4* dst = reinterpret_cast<uint4*>(qr + (bz * rows + r) * cols + cc);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      scr[(bz * rows + r) * (cols / 32) + cc / 32] = static_cast<uint8_t>(e + 127);
+      scr[scale_index(GROUPED, bz * rows + r, cc / 32, gridDim.z * rows, cols / 32)] = static_cast<uint8_t>(e + 127);
     }
   }
 }
@@ -212,29 +266,52 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
 }  // namespace
 
 void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sc,
-                    hipStream_t s) {
+                    hipStream_t s, bool grouped) {
   const int64_t nvec8 = rows * cols / 8;
   if (nvec8 == 0) return;
+  if (grouped) {
+    // cols % 128 == 0; the vector count fits 32 bits for the FFN's operands
+    const dim3 grid(static_cast<unsigned>(cdiv(nvec8, 256)));
+    if (src_dtype == MOE_F32)
+      MOE_LAUNCH("mx_quantize_rows", mx_rows_grouped_kernel<float>, grid, dim3(256), 0, s,
+                 static_cast<const float*>(src), static_cast<uint32_t>(nvec8), static_cast<uint32_t>(rows),
+                 static_cast<uint32_t>(cols / 128), q, sc);
+    else
+      MOE_LAUNCH("mx_quantize_rows", mx_rows_grouped_kernel<uint16_t>, grid, dim3(256), 0, s,
+                 static_cast<const uint16_t*>(src), static_cast<uint32_t>(nvec8), static_cast<uint32_t>(rows),
+                 static_cast<uint32_t>(cols / 128), q, sc);
+    return;
+  }
   const dim3 grid(static_cast<unsigned>(cdiv(nvec8, 256)));
   if (src_dtype == MOE_F32)
-    MOE_LAUNCH("mx_quantize_rows", mx_rows_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(src), nvec8, q, sc);
+    MOE_LAUNCH("mx_quantize_rows", mx_rows_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(src),
+               nvec8, q, sc);
   else
-    MOE_LAUNCH("mx_quantize_rows", mx_rows_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), nvec8, q,
-                       sc);
+    MOE_LAUNCH("mx_quantize_rows", mx_rows_kernel<uint16_t>, grid, dim3(256), 0, s,
+               static_cast<const uint16_t*>(src), nvec8, q, sc);
 }
 
 void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
-                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s) {
-  const int64_t nblk = seg ? cdiv(rows, 32) + nseg : rows / 32;
+                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s, bool grouped) {
+  const int64_t nblk = seg ? ldq / 32 : rows / 32;
   if (nblk == 0 || cols == 0 || batch == 0) return;
   const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
                   static_cast<unsigned>(batch));
-  if (src_dtype == MOE_F32)
-    MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false>), grid, dim3(256), 0, s,
-               static_cast<const float*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
-  else
-    MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false>), grid, dim3(256), 0, s,
-               static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+  if (src_dtype == MOE_F32) {
+    if (grouped)
+      MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false, true>), grid, dim3(256), 0, s,
+                 static_cast<const float*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+    else
+      MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false, false>), grid, dim3(256), 0, s,
+                 static_cast<const float*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+  } else {
+    if (grouped)
+      MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false, true>), grid, dim3(256), 0, s,
+                 static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+    else
+      MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false, false>), grid, dim3(256), 0, s,
+                 static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+  }
 }
 
 void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, uint8_t* qc,
@@ -244,10 +321,10 @@ void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows,
   const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
                   static_cast<unsigned>(batch));
   if (src_dtype == MOE_F32)
-    MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<float, true>), grid, dim3(256), 0, s,
+    MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<float, true, true>), grid, dim3(256), 0, s,
                static_cast<const float*>(src), rows, cols, nullptr, 0, rows, qc, sc, qr, scr);
   else
-    MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<uint16_t, true>), grid, dim3(256), 0, s,
+    MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<uint16_t, true, true>), grid, dim3(256), 0, s,
                static_cast<const uint16_t*>(src), rows, cols, nullptr, 0, rows, qc, sc, qr, scr);
 }
 
@@ -264,17 +341,17 @@ extern "C" int mx_quantize(const void* src, int src_dtype, int64_t batch, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (axis == 1) {
     if (seg_offsets || cols % 32) return MOE_EINVAL;
-    launch_mx_rows(src, src_dtype, batch * rows, cols, q, scales, s);
+    launch_mx_rows(src, src_dtype, batch * rows, cols, q, scales, s, false);
     return launch_status();
   }
   if (cols % 8) return MOE_EINVAL;
   if (seg_offsets) {
     if (batch != 1 || nseg < 1 || nseg > kMaxE) return MOE_EINVAL;
     const int64_t ldq = 32 * (cdiv(rows, 32) + nseg);
-    launch_mx_cols(src, src_dtype, 1, rows, cols, seg_offsets, nseg, ldq, q, scales, s);
+    launch_mx_cols(src, src_dtype, 1, rows, cols, seg_offsets, nseg, ldq, q, scales, s, false);
   } else {
     if (rows % 32) return MOE_EINVAL;
-    launch_mx_cols(src, src_dtype, batch, rows, cols, nullptr, 0, rows, q, scales, s);
+    launch_mx_cols(src, src_dtype, batch, rows, cols, nullptr, 0, rows, q, scales, s, false);
   }
   return launch_status();
 }

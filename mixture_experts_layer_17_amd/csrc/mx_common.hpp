@@ -48,18 +48,21 @@ __device__ __forceinline__ float mx_inv_scale(int e) {
   return n >= -126 ? __uint_as_float(static_cast<uint32_t>(n + 127) << 23) : __uint_as_float(0x00400000u);
 }
 
-// Launchers of the quantiser (mx.hip).
-//  rows layout: blocks along the contiguous axis; q [rows, cols], sc [rows, cols/32]
+// Launchers of the quantiser (mx.hip).  Scale layouts: the public one is
+// row-major [nrows, nblk]; with `grouped` (the MX GEMM operands; nblk % 4 == 0)
+// the scale of (row r, block b) is byte ((b/4) nrows + r) 4 + b%4, so a tile's
+// scales for one K-step of 128 elements are one contiguous run of 32-bit words.
+//  rows layout: blocks along the contiguous axis; q [rows, cols], scales of a [rows, cols/32] matrix
 void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sc,
-                    hipStream_t s);
-//  column layout: blocks run down the rows, stored transposed: q [batch][cols][ldq], sc [batch][cols][ldq/32].
-//  With seg (device, nseg+1 offsets; batch 1) blocks restart at each segment.
+                    hipStream_t s, bool grouped);
+//  column layout: blocks run down the rows, stored transposed: q [batch][cols][ldq], scales of a
+//  [batch][cols][ldq/32] matrix (grouped: each batch's [cols, ldq/32] matrix grouped).  With seg (device,
+//  nseg+1 offsets; batch 1) blocks restart at each segment.
 void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
-                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s);
-
-//  both layouts of a [batch, rows, cols] source from one read (no segments; rows % 32 == 0, cols % 32 == 0):
-//  column layout qc [batch][cols][rows], sc [batch][cols][rows/32] and row layout qr [batch][rows][cols],
-//  scr [batch][rows][cols/32].
+                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s, bool grouped);
+//  both layouts of a [batch, rows, cols] source from one read (no segments; rows % 128 == 0, cols % 128 == 0),
+//  grouped scales: column layout qc [batch][cols][rows] (scales grouped per batch) and row layout
+//  qr [batch][rows][cols] (scales of the [batch*rows, cols/32] matrix grouped).
 void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, uint8_t* qc,
                     uint8_t* sc, uint8_t* qr, uint8_t* scr, hipStream_t s);
 
