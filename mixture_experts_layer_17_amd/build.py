@@ -36,7 +36,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    extra = os.environ.get("MOE_HIPCC_DEFINES", "").split()  # e.g. -DMOE_BIG_TILE=2
+    extra = os.environ.get("MOE_HIPCC_DEFINES", "").split()  # extra hipcc flags for experiments, e.g. -DNAME=1
     cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -26,12 +26,6 @@
 // C[8(r/4) + 4(l/32) + r%4][l % 32].
 #include "gemm_common.hpp"
 
-#ifndef MOE_BIG_BK
-#define MOE_BIG_BK 64
-#endif
-#ifndef MOE_SMALL_BK
-#define MOE_SMALL_BK 64
-#endif
 
 namespace moe {
 namespace {
@@ -56,23 +50,10 @@ struct Cfg {
   static_assert(NA >= 2 && NA <= 3 && NB >= 2 && NB <= 3 && NA + NB <= 5, "LDS ring depth");
   static_assert(kLds * 2 <= 160 * 1024, "LDS budget");
 };
-#ifndef MOE_BIG_WN
-#define MOE_BIG_WN 4
-#endif
-#ifndef MOE_BIG_NA
-#define MOE_BIG_NA 2
-#endif
-#ifndef MOE_BIG_NB
-#define MOE_BIG_NB 2
-#endif
-#ifndef MOE_SMALL_NA
-#define MOE_SMALL_NA 3
-#endif
-#ifndef MOE_SMALL_NB
-#define MOE_SMALL_NB 2
-#endif
-using Big = Cfg<256, 256, 2, MOE_BIG_WN, MOE_BIG_BK, MOE_BIG_NA, MOE_BIG_NB>;
-using Small = Cfg<128, 128, 2, 2, MOE_SMALL_BK, MOE_SMALL_NA, MOE_SMALL_NB>;
+// 256 x 256, 8 waves of 128 x 64, K step 64, two stages per operand
+using Big = Cfg<256, 256, 2, 4, 64, 2, 2>;
+// 128 x 128, 4 waves of 64 x 64, K step 64, three A stages (two workgroups per CU)
+using Small = Cfg<128, 128, 2, 2, 64, 3, 2>;
 // 128 x 256, 8 waves of 64 x 64, K step 32: two workgroups per CU (short segments, forward GEMMs)
 using Mid = Cfg<128, 256, 2, 4, 32, 3, 2>;
 
@@ -211,9 +192,6 @@ __device__ __forceinline__ bf16x8 frag_b(const uint16_t* Bs, int wn, int j, int 
   }
 }
 
-#ifndef MOE_FRAG_PIPE
-#define MOE_FRAG_PIPE 0
-#endif
 template <class C, bool AKC, bool BKC, bool BDUAL>
 __device__ __forceinline__ void load_frags(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int ks, int lane,
                                            bf16x8* a, bf16x8* b) {
@@ -227,33 +205,6 @@ __device__ __forceinline__ void load_frags(const uint16_t* As, const uint16_t* B
 template <class C, bool AKC, bool BKC, bool BDUAL>
 __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs, int wm,
                                           int wn, int lane, Acc<C>& acc) {
-#if MOE_FRAG_PIPE
-  // fragments of k-slice ks+1 are read while the MFMAs of slice ks run
-  bf16x8 a[2][C::TM], b[2][C::TN];
-  load_frags<C, AKC, BKC, BDUAL>(As, Bs, wm, wn, 0, lane, a[0], b[0]);
-#pragma unroll
-  for (int ks = 0; ks < C::BK / 16; ++ks) {
-    const int c = ks & 1;
-    if (ks + 1 < C::BK / 16) load_frags<C, AKC, BKC, BDUAL>(As, Bs, wm, wn, ks + 1, lane, a[c ^ 1], b[c ^ 1]);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-#if MOE_FRAG_PIPE == 2
-    if (ks + 1 < C::BK / 16) {
-      // one LDS read between consecutive MFMAs
-      constexpr int nr = C::TM * (AKC ? 1 : 2) + C::TN * (BKC ? 1 : 2);
-      constexpr int nm = C::TM * C::TN;
-#pragma unroll
-      for (int t = 0; t < (nr > nm ? nr : nm); ++t) {
-        if (t < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (t < nm) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    }
-#endif
-  }
-#else
 #pragma unroll
   for (int ks = 0; ks < C::BK / 16; ++ks) {
     bf16x8 a[C::TM], b[C::TN];
@@ -264,7 +215,6 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const
       for (int j = 0; j < C::TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
-#endif
 }
 
 // C = A B over K = [0, K).  K-step kt of A lives in A slot kt % NA and of B in
