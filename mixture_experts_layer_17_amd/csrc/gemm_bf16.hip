@@ -312,7 +312,8 @@ __global__ __launch_bounds__(C::kThreads) void ffn_bf16_kernel(FfnArgs p) {
       const KcOp a{static_cast<const uint16_t*>(p.act) + row0 * f, nullptr, f, kNoSplit, rows};
       const McOp b{Wd + e * wsz, nullptr, d, n0, f};
       mainloop<C, true, false, false>(a, b, f, lds, tid, acc);
-      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
+      // Y is read by the combine right after: ordinary (cached) stores
+      epi_store<C, false>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
       const int n0 = nt * C::BN;  // over f
       const KcOp a{static_cast<const uint16_t*>(p.dy) + row0 * d, nullptr, d, kNoSplit, rows};

@@ -63,14 +63,18 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
 
 // Copy a rows x cols bf16 tile from LDS (row stride ldc) to global memory with
 // 16-byte stores; only rows < rows_valid and columns < cols_valid are written.
-template <class C>
+// NT: streaming (non-temporal) stores, for outputs the next kernel does not read.
+template <class C, bool NT = true>
 __device__ __forceinline__ void flush_tile(const uint16_t* ct, int ldc, int rows, int cols, uint16_t* dst,
                                            int64_t ld, int rows_valid, int cols_valid, int tid) {
   const int cpr = cols / 8;
   for (int c = tid; c < rows * cpr; c += C::kThreads) {
     const int r = c / cpr, cc = (c % cpr) * 8;
-    if (r < rows_valid && cc < cols_valid)
-      *reinterpret_cast<uint4*>(dst + r * ld + cc) = *reinterpret_cast<const uint4*>(ct + r * ldc + cc);
+    if (r < rows_valid && cc < cols_valid) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ct + r * ldc + cc);
+      if constexpr (NT) store16_nt(dst + r * ld + cc, v);
+      else *reinterpret_cast<uint4*>(dst + r * ld + cc) = v;
+    }
   }
 }
 
@@ -87,7 +91,7 @@ __device__ __forceinline__ void load_tile(uint16_t* ct, int ldc, int rows, int c
 }
 
 // Store the plain accumulator tile (bf16) to dst[r*ld + c].
-template <class C>
+template <class C, bool NT = true>
 __device__ __forceinline__ void epi_store(const Acc<C>& acc, uint16_t* lds, uint16_t* dst, int64_t ld,
                                           int rows_valid, int cols_valid, int tid) {
   constexpr int ldc = C::BN + 8;
@@ -103,7 +107,7 @@ __device__ __forceinline__ void epi_store(const Acc<C>& acc, uint16_t* lds, uint
         lds[acc_row<C>(wm, i, r, lane) * ldc + acc_col<C>(wn, j, lane)] =
             static_cast<uint16_t>(f32_to_bf16(acc[i][j][r]));
   __syncthreads();
-  flush_tile<C>(lds, ldc, C::BM, C::BN, dst, ld, rows_valid, cols_valid, tid);
+  flush_tile<C, NT>(lds, ldc, C::BM, C::BN, dst, ld, rows_valid, cols_valid, tid);
 }
 
 // G1 epilogue: Hg and Hu tiles (BM x BN/2 each: the gate columns are

@@ -275,7 +275,8 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
       const int64_t so = e * wsz / 32 + static_cast<int64_t>(n0) * 4;  // scales grouped per expert over d rows
       const MxKc b{m.wdq + wo, nullptr, m.wds + so, nullptr, f, 0, f, kNoSplit, d - n0, static_cast<int64_t>(d) * 4};
       mx_mainloop<C, false>(a, b, f, lds8, tid, acc);
-      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
+      // Y is read by the combine right after: ordinary (cached) stores
+      epi_store<C, false>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
       const int n0 = nt * C::BN;  // over f
       const MxKc a{m.dyq + row0 * d, nullptr, m.dys + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, p.R * 4};

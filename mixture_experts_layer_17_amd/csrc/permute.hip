@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64 * kWaves) void dispatch_kernel(const T* __restri
 #pragma unroll
       for (int i = 0; i < kMaxChunks; ++i) {
         const int c = c0 + i * 64 + lane;
-        if (c < nvec) dst[c] = v[i];
+        if (c < nvec) store16_nt(dst + c, v[i]);
       }
     }
   }
