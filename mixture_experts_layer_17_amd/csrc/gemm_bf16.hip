@@ -395,6 +395,8 @@ int launch_cfg(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s) {
 // segment holds at least four such tiles, else 128 (Small and Mid share it).
 bool big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 1024; }
 // Weight-gradient tiles: 256 x 256 when d and f fill them.
+// (128 x 128 tiles for short token segments measured slower: the 256 x 256
+// tile's reuse outweighs its unoverlapped epilogue.)
 bool big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
 
 }  // namespace
