@@ -72,8 +72,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// The reciprocal is the hardware approximation (v_rcp_f32, about 1 ulp), not
+// an IEEE division; exp(-z) overflowing to infinity gives 0 as it should.
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
 // ---------------------------------------------------------------------------
 // Launch wrapper: optionally brackets each launch with timing events (timing.hip).

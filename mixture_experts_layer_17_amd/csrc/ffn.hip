@@ -82,21 +82,9 @@ int tile_bm(int prec, int64_t R, int E) {
 
 size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }
 
-// Workspace layout: [tile table][G3 tile table (bf16 backward, see below)][dHg][dHu] (backward only)
-// [MX scratch] (MXFP8 only).
-// bf16 backward: the SwiGLU-backward GEMM (G3) walks 128-row tiles of its own
-// when the others use 256-row ones (its epilogue then overlaps the other
-// workgroup's main loop on the same CU).
-bool g3_own_table(const FfnShape& s) { return s.prec == MOE_BF16 && tile_bm(s.prec, s.R, s.E) != 128; }
-
-size_t one_table_bytes(int64_t R, int E, int bm) {
-  return align_up(static_cast<size_t>(max_m_tiles(R, E, bm) + 1) * sizeof(int4), 256);
-}
-
+// Workspace layout: [tile table][dHg][dHu] (backward only)[MX scratch] (MXFP8 only).
 size_t tiles_bytes(const FfnShape& s) {
-  size_t b = one_table_bytes(s.R, s.E, tile_bm(s.prec, s.R, s.E));
-  if (g3_own_table(s)) b += one_table_bytes(s.R, s.E, 128);
-  return b;
+  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec, s.R, s.E)) + 1) * sizeof(int4), 256);
 }
 
 size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {
@@ -107,6 +95,28 @@ size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {
 }
 
 }  // namespace
+
+int occupancy(const void* kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) n = 1;
+  return n < 1 ? 1 : n;
+}
+
+unsigned persistent_grid(int occ, int64_t work) {
+  constexpr int kMaxDev = 64;
+  static int cus[kMaxDev] = {};  // compute units per device, looked up once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int n = dev < kMaxDev ? __atomic_load_n(&cus[dev], __ATOMIC_RELAXED) : 0;
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = kNumXcd;
+    if (dev < kMaxDev) __atomic_store_n(&cus[dev], n, __ATOMIC_RELAXED);
+  }
+  int64_t g = static_cast<int64_t>(n) * occ / kNumXcd * kNumXcd;
+  if (g < kNumXcd) g = kNumXcd;
+  const int64_t w = static_cast<int64_t>(xcd_grid(work < 1 ? 1 : work));
+  return static_cast<unsigned>(g < w ? g : w);
+}
 
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
                      hipStream_t s) {
@@ -233,17 +243,7 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
   int st = MOE_OK;
   if (R > 0) {
-    if (g3_own_table(sh)) {
-      FfnArgs a3 = a;
-      a3.bm = 128;
-      a3.max_tiles = max_m_tiles(R, E, 128);
-      int4* t3 = reinterpret_cast<int4*>(wsb + one_table_bytes(R, E, bm));
-      a3.tiles = t3;
-      launch_tile_map(offsets, E, 128, R, a3.max_tiles, t3, s);
-      st = launch(kG3, a3, a3.max_tiles, s);
-    } else {
-      st = launch(kG3, a, mt, s);
-    }
+    st = launch(kG3, a, mt, s);
     if (st == MOE_OK) st = launch(kG5, a, mt, s);
   }
   if (st == MOE_OK) st = launch(kG4, a, mt, s);

@@ -85,6 +85,13 @@ __device__ __forceinline__ bool wgrad_tile(int64_t h, int E, int gm, int gn, int
   return true;
 }
 
+// Persistent launches (ffn.hip).  occupancy: resident workgroups per compute
+// unit of `kernel` at `threads` per workgroup (at least 1).  persistent_grid:
+// compute units x occ of the current device, rounded down to a multiple of the
+// XCD count, and at most xcd_grid(work).
+int occupancy(const void* kernel, int threads);
+unsigned persistent_grid(int occ, int64_t work);
+
 // Launch the tile-table builder (defined in ffn.hip).
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
                      hipStream_t s);

@@ -198,5 +198,157 @@ __device__ __forceinline__ void epi_swiglu_bwd(const Acc<C>& acc, uint16_t* lds,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Register-direct epilogues.  The kernels using them compute every 32 x 32
+// tile transposed, as mfma(B fragment, A fragment): then register r of lane l
+// holds C[l % 32][8(r/4) + 4(l/32) + r%4], four consecutive columns of one
+// row.  to_chunks exchanges halves between lanes l and l + 32
+// (v_permlane32_swap) so that each lane holds two runs of eight: chunk c of
+// lane l is row l % 32, columns 16c + 8(l/32) .. +7, stored as one 16-byte
+// vector.  No LDS and no barrier: the next tile's loads can be in flight.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void to_chunks(const f32x16& a, float (&o)[2][8]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * c + s]),
+                                                      __float_as_uint(a[8 * c + 4 + s]), false, false);
+      o[c][s] = __uint_as_float(r[0]);
+      o[c][4 + s] = __uint_as_float(r[1]);
+    }
+}
+
+__device__ __forceinline__ uint4 pack8(const float* v) {
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint16_t* p, const uint4& v) {
+  if constexpr (NT) store16_nt(p, v);
+  else *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Plain bf16 output tile at dst (row stride ld): rows < rows_valid, columns < cols_valid.
+// Ordinary (cached) stores: each instruction writes 32 bytes of 32 rows, and the
+// L2 merges them into whole lines (streaming stores of such pieces measured slower).
+template <class C, bool NT = false>
+__device__ __forceinline__ void epi_regs_store(const Acc<C>& acc, uint16_t* dst, int64_t ld, int rows_valid,
+                                               int cols_valid, int lane, int wm, int wn) {
+  const int rl = lane & 31, hc = 8 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WTM + i * 32 + rl;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      float v[2][8];
+      to_chunks(acc[i][j], v);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int col = wn * C::WTN + j * 32 + 16 * c + hc;
+        if (row < rows_valid && col < cols_valid) store16<NT>(dst + row * ld + col, pack8(v[c]));
+      }
+    }
+  }
+}
+
+// G1: gate tiles j < TN/2 and up tiles j >= TN/2 cover the same f columns;
+// stores Hg, Hu and A = silu(Hg) * Hu (SwiGLU, from the fp32 accumulators).
+template <class C>
+__device__ __forceinline__ void epi_regs_swiglu_fwd(const Acc<C>& acc, const FfnArgs& p, int64_t row0, int rows,
+                                                    int n0, int lane, int wm, int wn) {
+  constexpr int H = C::TN / 2;
+  const int rl = lane & 31, hc = 8 * (lane >> 5);
+  const int64_t f = p.f;
+  uint16_t* hg = static_cast<uint16_t*>(p.o_hg) + row0 * f + n0;
+  uint16_t* hu = static_cast<uint16_t*>(p.o_hu) + row0 * f + n0;
+  uint16_t* ac = static_cast<uint16_t*>(p.o_act) + row0 * f + n0;
+  const int cols = p.f - n0;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WTM + i * 32 + rl;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      float g[2][8], u[2][8];
+      to_chunks(acc[i][j], g);
+      to_chunks(acc[i][j + H], u);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int col = wn * (C::WTN / 2) + j * 32 + 16 * c + hc;
+        if (row < rows && col < cols) {
+          float a[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) a[t] = silu_f(g[c][t]) * u[c][t];
+          const int64_t o = row * f + col;
+          store16<false>(hg + o, pack8(g[c]));
+          store16<false>(hu + o, pack8(u[c]));
+          store16<false>(ac + o, pack8(a));
+        }
+      }
+    }
+  }
+}
+
+// G3: SwiGLU backward from dA (the accumulators) and the stored Hg, Hu:
+// dHu = dA * silu(Hg), dHg = dA * Hu * silu'(Hg), stored as bf16.  The Hg, Hu
+// chunks of row block i + 1 are loaded while block i is computed, and all loads
+// of a block precede its stores (which could alias them as far as the compiler
+// knows), so the load latencies overlap.
+template <class C>
+__device__ __forceinline__ void epi_regs_swiglu_bwd(const Acc<C>& acc, const FfnArgs& p, int64_t row0, int rows,
+                                                    int n0, int lane, int wm, int wn) {
+  const int rl = lane & 31, hc = 8 * (lane >> 5);
+  const int64_t f = p.f;
+  const uint16_t* hg = static_cast<const uint16_t*>(p.hg) + row0 * f + n0;
+  const uint16_t* hu = static_cast<const uint16_t*>(p.hu) + row0 * f + n0;
+  uint16_t* dg = static_cast<uint16_t*>(p.o_dhg) + row0 * f + n0;
+  uint16_t* du = static_cast<uint16_t*>(p.o_dhu) + row0 * f + n0;
+  const int cols = p.f - n0;
+  auto load = [&](int i, uint4 (&lg)[C::TN][2], uint4 (&lu)[C::TN][2]) {
+    const int row = wm * C::WTM + i * 32 + rl;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int col = wn * C::WTN + j * 32 + 16 * c + hc;
+        const bool ok = row < rows && col < cols;
+        const int64_t o = row * f + col;
+        lg[j][c] = ok ? *reinterpret_cast<const uint4*>(hg + o) : make_uint4(0, 0, 0, 0);
+        lu[j][c] = ok ? *reinterpret_cast<const uint4*>(hu + o) : make_uint4(0, 0, 0, 0);
+      }
+  };
+  uint4 lg[2][C::TN][2], lu[2][C::TN][2];
+  load(0, lg[0], lu[0]);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WTM + i * 32 + rl;
+    if (i + 1 < C::TM) load(i + 1, lg[(i + 1) & 1], lu[(i + 1) & 1]);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      float da[2][8];
+      to_chunks(acc[i][j], da);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int col = wn * C::WTN + j * 32 + 16 * c + hc;
+        if (row < rows && col < cols) {
+          const int64_t o = row * f + col;
+          float g[8], u[8], og[8], ou[8];
+          Elem<uint16_t>::unpack(lg[i & 1][j][c], g);
+          Elem<uint16_t>::unpack(lu[i & 1][j][c], u);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float sg = sigmoid_f(g[t]);
+            ou[t] = da[c][t] * g[t] * sg;
+            og[t] = da[c][t] * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
+          }
+          store16<false>(dg + o, pack8(og));
+          store16<false>(du + o, pack8(ou));
+        }
+      }
+    }
+  }
+}
+
 }  // namespace gemm
 }  // namespace moe
