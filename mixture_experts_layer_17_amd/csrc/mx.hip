@@ -59,11 +59,8 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const T* __restrict__ src,
   const int e = mx_block_exponent(amax);
   const float inv = mx_inv_scale(e);
   if (!ok) return;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lo |= e4m3_encode(v[j] * inv) << (8 * j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hi |= e4m3_encode(v[4 + j] * inv) << (8 * j);
+  const uint32_t lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  const uint32_t hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
   reinterpret_cast<uint2*>(q)[i] = make_uint2(lo, hi);
   if ((i & 3) == 0) sc[i >> 2] = static_cast<uint8_t>(e + 127);
 }
@@ -96,11 +93,8 @@ __global__ __launch_bounds__(256) void mx_rows_grouped_kernel(const T* __restric
   sw |= __shfl_xor(sw, 4, 64);
   sw |= __shfl_xor(sw, 8, 64);
   if (!ok) return;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lo |= e4m3_encode(v[j] * inv) << (8 * j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hi |= e4m3_encode(v[4 + j] * inv) << (8 * j);
+  const uint32_t lo = e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  const uint32_t hi = e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
   reinterpret_cast<uint2*>(q)[i] = make_uint2(lo, hi);
   if ((i & 15) == 0) {
     const uint32_t gg = i >> 4, r = gg / ngpr, G = gg - r * ngpr;
@@ -200,10 +194,8 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     const float inv = mx_inv_scale(e);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) w |= e4m3_encode(v[4 * k + t] * inv) << (8 * t);
-      obuf[lane][wave * 8 + k] = w;
+      obuf[lane][wave * 8 + k] =
+          e4m3_pack4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
     }
     osc[lane][wave] = static_cast<uint8_t>(e + 127);
   }
@@ -250,11 +242,8 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
       const float inv = mx_inv_scale(e);
       uint32_t w[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        w[k] = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) w[k] |= e4m3_encode(v[4 * k + t] * inv) << (8 * t);
-      }
+      for (int k = 0; k < 8; ++k)
+        w[k] = e4m3_pack4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
       uint4* dst = reinterpret_cast<uint4*>(qr + (bz * rows + r) * cols + cc);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);

@@ -180,6 +180,43 @@ def test_mx_quantize_cols_batched_bit_exact(gpu, dtype):
         np.testing.assert_array_equal(s[b].cpu().numpy(), rs.T)
 
 
+def _e4m3_rounding_cases(seed=11):
+    """fp32 values below 512 in magnitude around every E4M3 rounding decision:
+    each grid value and each midpoint between neighbours (ties to even), the
+    saturation range above 448, the subnormal floor 2^-10, three fp32 ulps to
+    either side of all of those, both signs; plus random fp32 patterns."""
+    g = mxo.e4m3_decode(np.arange(0x7F))
+    pts = np.concatenate([g, (g[:-1] + g[1:]) / 2, [456.0, 464.0, 480.0, 500.0, 2.0 ** -10, 1.5 * 2.0 ** -10]])
+    u = pts.astype(np.float32).view(np.uint32).astype(np.int64)
+    near = (u[:, None] + np.arange(-3, 4)[None, :]).reshape(-1)
+    near = near[(near >= 0) & (near < 0x44000000)]
+    rnd = np.random.default_rng(seed).integers(0, 0x44000000, 1 << 20)
+    bits = np.concatenate([near, rnd]).astype(np.uint32)
+    sign = np.random.default_rng(seed + 1).integers(0, 2, bits.size).astype(np.uint32) << 31
+    both = np.concatenate([bits, bits | np.uint32(0x80000000), bits ^ sign])
+    return both.view(np.float32)
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+def test_mx_quantize_rounding_boundaries(gpu, axis):
+    """Blocks [256, 31 cases]: the block exponent is 0, so every case is encoded
+    unscaled; codes and scales bit-exact against the oracle."""
+    vals = _e4m3_rounding_cases()
+    nblk = -(-vals.size // 31 // 8) * 8  # the column layout wants a multiple of 8 columns
+    blocks = np.zeros((nblk, 32), np.float32)
+    blocks[:, 0] = 256.0
+    blocks.reshape(-1)[np.flatnonzero(np.arange(nblk * 32) % 32)[:vals.size]] = vals
+    m = blocks if axis == 1 else np.ascontiguousarray(blocks.T)
+    q, s = B.mx_quantize(torch.from_numpy(m).cuda(), axis=axis)
+    torch.cuda.synchronize()
+    rq, rs = mxo.mx_quantize(m.astype(np.float64), axis=axis)
+    assert np.all(rs == 127)
+    if axis == 0:
+        rq, rs = rq.T, rs.T  # stored transposed
+    np.testing.assert_array_equal(q[0].cpu().numpy(), rq)
+    np.testing.assert_array_equal(s[0].cpu().numpy(), rs)
+
+
 def test_mx_quantize_segments_bit_exact(gpu):
     t, v = _mx_input((500, 136), 3, torch.bfloat16)
     seg = np.array([0, 0, 45, 45, 77, 300, 301, 500], np.int32)
