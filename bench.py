@@ -209,7 +209,8 @@ def main() -> int:
     w = wl.WORKLOADS[args.workload]
     print(f"# workload {w.name} {w.describe()}: generating inputs", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed=args.seed)
-    step = L.LayerStep(w, L.to_device(inp))
+    # MXFP8: each step quantises the expert weights once, into both layouts, for its forward and backward
+    step = L.LayerStep(w, L.to_device(inp), mx_weights_per_step=True)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
@@ -303,29 +304,27 @@ def main() -> int:
                           "max_over_mean": rs[0] * w.E / max(rs[3], 1)},
     }
     if w.prec == "mxfp8":
-        # the same step on pre-quantised weights (moe_mx_weight_cache_build): the weights are quantised once per
-        # optimiser step, so a loop with several micro-batches per step pays this rate plus build_ms / micro-batches
+        # the other two ways of handling the weights, same buffers and inputs
         b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        step.build_weight_cache()  # warm
-        torch.cuda.synchronize()
         b0.record()
         step.build_weight_cache()
         b1.record()
         torch.cuda.synchronize()
         build_ms = b0.elapsed_time(b1)
-        for _ in range(args.warmup):
-            step.step()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            step.step()
-        stop.record()
-        torch.cuda.synchronize()
-        ms_c = start.elapsed_time(stop) / args.steps
-        line["mx_weight_cache"] = {
-            "tokens_per_s": w.T / (ms_c * 1e-3), "ms_per_step": ms_c, "build_ms": build_ms,
-            "note": "same step with expert weights quantised once by moe_mx_weight_cache_build (excluded); "
-                    "value above quantises every weight in every step"}
+        step.mx_per_step = False
+        ms_once = timed_steps(step, args.steps, args.warmup)   # cache built above, reused
+        cache, step.mx_wcache = step.mx_wcache, None
+        ms_pass = timed_steps(step, args.steps, args.warmup)   # forward and backward quantise their own layouts
+        step.mx_wcache, step.mx_per_step = cache, True
+        line["mx_weights"] = {
+            "value": "expert weights quantised at the start of every step into both layouts from one read "
+                     "(moe_mx_weight_cache_build, inside the timed step) and used by its forward and backward",
+            "build_ms": build_ms,
+            "per_pass": {"tokens_per_s": w.T / (ms_pass * 1e-3), "ms_per_step": ms_pass,
+                         "note": "forward and backward each quantise the weight layout they use (no cache)"},
+            "once": {"tokens_per_s": w.T / (ms_once * 1e-3), "ms_per_step": ms_once,
+                     "note": "weights quantised once before the loop and reused (build excluded): the rate of "
+                             "micro-batches that share one optimiser step"}}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

@@ -500,9 +500,9 @@ int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* sc
     const WCache w = carve_wcache(cc, a.E, a.d, a.f);
     m.wgq = w.wg_f.q; m.wgs = w.wg_f.s; m.wuq = w.wu_f.q; m.wus = w.wu_f.s; m.wdq = w.wd_f.q; m.wds = w.wd_f.s;
   } else {
-    launch_mx_cols(a.wg, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wg.q, b.wg.s, s, true);
-    launch_mx_cols(a.wu, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wu.q, b.wu.s, s, true);
-    launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s, true);
+    launch_mx_cols(a.wg, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wg.q, b.wg.s, s, true, nullptr);
+    launch_mx_cols(a.wu, bf, a.E, a.d, a.f, nullptr, 0, a.d, b.wu.q, b.wu.s, s, true, nullptr);
+    launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s, true, nullptr);
     m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s; m.wdq = b.wd.q; m.wds = b.wd.s;
   }
   m.xq = b.x.q; m.xs = b.x.s;
@@ -551,11 +551,11 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
     st = launch_mx_kind(kG5, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // weight gradients: every operand along tokens, per expert segment, transposed
-    launch_mx_cols(a.act, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.at.q, b.at.s, s, true);
-    launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s, true);
-    launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s, true);
-    launch_mx_cols(a.dhg, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhgt.q, b.dhgt.s, s, true);
-    launch_mx_cols(a.dhu, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhut.q, b.dhut.s, s, true);
+    launch_mx_cols(a.act, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.at.q, b.at.s, s, true, mx_blk_offsets);
+    launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s, true, mx_blk_offsets);
+    launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s, true, mx_blk_offsets);
+    launch_mx_cols(a.dhg, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhgt.q, b.dhgt.s, s, true, mx_blk_offsets);
+    launch_mx_cols(a.dhu, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhut.q, b.dhut.s, s, true, mx_blk_offsets);
   }
   m.atq = b.at.q; m.ats = b.at.s; m.dytq = b.dyt.q; m.dyts = b.dyt.s;
   m.xtq = b.xt.q; m.xts = b.xt.s;

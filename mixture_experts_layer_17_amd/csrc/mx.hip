@@ -115,7 +115,8 @@ constexpr int kColW = 64;
 // serves both orientations).
 template <typename T, bool BOTH, bool GROUPED>
 __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
-                                                     const int32_t* __restrict__ seg, int nseg, int64_t ldq,
+                                                     const int32_t* __restrict__ seg, const int32_t* __restrict__ blk,
+                                                     int nseg, int64_t ldq,
                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
                                                      uint8_t* __restrict__ qr, uint8_t* __restrict__ scr) {
   constexpr int VEC = 16 / sizeof(T);       // elements per 16-byte vector
@@ -133,16 +134,27 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
   const int64_t nblk = seg ? ldq / 32 : rows / 32;
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 4;
   if (seg) {
+    // segment offsets and the prefix sum of their 32-row block counts: given
+    // (blk), or an inclusive scan over one thread per segment
+    static_assert(kMaxE == 256, "one thread per segment");
     for (int i = tid; i <= nseg; i += blockDim.x) s_off[i] = seg[i];
-    __syncthreads();
-    if (tid == 0) {
-      int32_t run = 0;
-      s_blk[0] = 0;
-      for (int i = 0; i < nseg; ++i) {
-        int32_t n = s_off[i + 1] - s_off[i];
-        if (n < 0) n = 0;
-        run += (n + 31) / 32;
-        s_blk[i + 1] = run;
+    if (blk) {
+      for (int i = tid; i <= nseg; i += blockDim.x) s_blk[i] = blk[i];
+    } else {
+      __syncthreads();
+      int32_t c = 0;
+      if (tid < nseg) {
+        const int32_t n = s_off[tid + 1] - s_off[tid];
+        c = n > 0 ? (n + 31) / 32 : 0;
+      }
+      s_blk[tid + 1] = c;
+      if (tid == 0) s_blk[0] = 0;
+      __syncthreads();
+      for (int o = 1; o < kMaxE; o <<= 1) {
+        const int32_t v = tid >= o ? s_blk[tid + 1 - o] : 0;
+        __syncthreads();
+        s_blk[tid + 1] += v;
+        __syncthreads();
       }
     }
     __syncthreads();
@@ -281,7 +293,7 @@ void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, 
 }
 
 void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
-                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s, bool grouped) {
+                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s, bool grouped, const int32_t* blk) {
   const int64_t nblk = seg ? ldq / 32 : rows / 32;
   if (nblk == 0 || cols == 0 || batch == 0) return;
   const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
@@ -289,17 +301,17 @@ void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows,
   if (src_dtype == MOE_F32) {
     if (grouped)
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false, true>), grid, dim3(256), 0, s,
-                 static_cast<const float*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const float*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
     else
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false, false>), grid, dim3(256), 0, s,
-                 static_cast<const float*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const float*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
   } else {
     if (grouped)
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false, true>), grid, dim3(256), 0, s,
-                 static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const uint16_t*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
     else
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false, false>), grid, dim3(256), 0, s,
-                 static_cast<const uint16_t*>(src), rows, cols, seg, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const uint16_t*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
   }
 }
 
@@ -311,10 +323,10 @@ void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows,
                   static_cast<unsigned>(batch));
   if (src_dtype == MOE_F32)
     MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<float, true, true>), grid, dim3(256), 0, s,
-               static_cast<const float*>(src), rows, cols, nullptr, 0, rows, qc, sc, qr, scr);
+               static_cast<const float*>(src), rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
   else
     MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<uint16_t, true, true>), grid, dim3(256), 0, s,
-               static_cast<const uint16_t*>(src), rows, cols, nullptr, 0, rows, qc, sc, qr, scr);
+               static_cast<const uint16_t*>(src), rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
 }
 
 }  // namespace moe
@@ -337,10 +349,10 @@ extern "C" int mx_quantize(const void* src, int src_dtype, int64_t batch, int64_
   if (seg_offsets) {
     if (batch != 1 || nseg < 1 || nseg > kMaxE) return MOE_EINVAL;
     const int64_t ldq = 32 * (cdiv(rows, 32) + nseg);
-    launch_mx_cols(src, src_dtype, 1, rows, cols, seg_offsets, nseg, ldq, q, scales, s, false);
+    launch_mx_cols(src, src_dtype, 1, rows, cols, seg_offsets, nseg, ldq, q, scales, s, false, nullptr);
   } else {
     if (rows % 32) return MOE_EINVAL;
-    launch_mx_cols(src, src_dtype, batch, rows, cols, nullptr, 0, rows, q, scales, s, false);
+    launch_mx_cols(src, src_dtype, batch, rows, cols, nullptr, 0, rows, q, scales, s, false, nullptr);
   }
   return launch_status();
 }

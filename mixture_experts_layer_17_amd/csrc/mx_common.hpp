@@ -56,9 +56,11 @@ void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, 
                     hipStream_t s, bool grouped);
 //  column layout: blocks run down the rows, stored transposed: q [batch][cols][ldq], scales of a
 //  [batch][cols][ldq/32] matrix (grouped: each batch's [cols, ldq/32] matrix grouped).  With seg (device,
-//  nseg+1 offsets; batch 1) blocks restart at each segment.
+//  nseg+1 offsets; batch 1) blocks restart at each segment; blk (device, nseg+1, or NULL) is the prefix sum
+//  of the segments' 32-row block counts when the caller has it.
 void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, const int32_t* seg,
-                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s, bool grouped);
+                    int nseg, int64_t ldq, uint8_t* q, uint8_t* sc, hipStream_t s, bool grouped,
+                    const int32_t* blk);
 //  both layouts of a [batch, rows, cols] source from one read (no segments; rows % 128 == 0, cols % 128 == 0),
 //  grouped scales: column layout qc [batch][cols][rows] (scales grouped per batch) and row layout
 //  qr [batch][rows][cols] (scales of the [batch*rows, cols/32] matrix grouped).

@@ -30,12 +30,22 @@ def to_device(inp: dict, device="cuda") -> dict:
 
 
 class LayerStep:
-    """Preallocated buffers and workspaces for one layer step of workload ``w``."""
+    """Preallocated buffers and workspaces for one layer step of workload ``w``.
 
-    def __init__(self, w: Workload, dev_inputs: dict, mx_weight_cache: bool = False):
+    MXFP8 expert weights, three ways:
+      default               the forward and the backward quantise the layouts they use (no cache);
+      mx_weights_per_step   every step first quantises the weights into both layouts from one read
+                            (moe_mx_weight_cache_build), and its forward and backward use them: the weights
+                            change once per optimiser step, so this is the whole per-step conversion;
+      mx_weight_cache       quantised once here and reused by every step (valid while the weights do not change).
+    """
+
+    def __init__(self, w: Workload, dev_inputs: dict, mx_weight_cache: bool = False,
+                 mx_weights_per_step: bool = False):
         self.w = w
         self.inp = dev_inputs
         self.mx_wcache = None
+        self.mx_per_step = bool(mx_weights_per_step) and w.prec == "mxfp8"
         x = dev_inputs["x"]
         dev = x.device
         T, d, E, k, f, R = w.T, w.d, w.E, w.k, w.f, w.R
@@ -73,11 +83,11 @@ class LayerStep:
         if self.linear_router:
             self.dw_router = torch.empty_like(dev_inputs["w_router"])
             self.router_ws = B._ws(B.lib().moe_router_logits_bwd_workspace(T, d, E), dev)
-        if mx_weight_cache and w.prec == "mxfp8":
+        if (mx_weight_cache or self.mx_per_step) and w.prec == "mxfp8":
             self.build_weight_cache()
 
     def build_weight_cache(self):
-        """Quantise the expert weights once (both orientations); later steps quantise no weight."""
+        """Quantise the expert weights (both orientations) into the cache the forward and backward read."""
         inp = self.inp
         self.mx_wcache = B.moe_mx_weight_cache_build(inp["w_gate"], inp["w_up"], inp["w_down"], cache=self.mx_wcache)
         return self.mx_wcache
@@ -110,5 +120,7 @@ class LayerStep:
         return self.dx
 
     def step(self):
+        if self.mx_per_step:
+            self.build_weight_cache()
         self.forward()
         self.backward()

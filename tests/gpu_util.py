@@ -52,8 +52,9 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def run_gpu_step(w: wl.Workload, inp: dict, mx_weight_cache: bool = False) -> tuple[dict, L.LayerStep]:
-    step = L.LayerStep(w, L.to_device(inp), mx_weight_cache=mx_weight_cache)
+def run_gpu_step(w: wl.Workload, inp: dict, mx_weight_cache: bool = False,
+                 mx_weights_per_step: bool = False) -> tuple[dict, L.LayerStep]:
+    step = L.LayerStep(w, L.to_device(inp), mx_weight_cache=mx_weight_cache, mx_weights_per_step=mx_weights_per_step)
     step.step()
     torch.cuda.synchronize()
     res = {k: host(v) for k, v in step.route.items()}

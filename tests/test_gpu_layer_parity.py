@@ -74,8 +74,11 @@ def test_mx_weight_cache_bit_identical(gpu, name):
     a, _ = gu.run_gpu_step(w, inp)
     b, step = gu.run_gpu_step(w, inp, mx_weight_cache=True)
     assert step.mx_wcache is not None
+    c, step_c = gu.run_gpu_step(w, inp, mx_weights_per_step=True)  # rebuilt inside the step
+    assert step_c.mx_wcache is not None
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+        np.testing.assert_array_equal(a[key], c[key], err_msg=key)
 
 
 def _sampled_full(w, n_tok=48, seed=0):
