@@ -84,11 +84,14 @@ def kernel_work(name: str, w, s: int) -> tuple[str, float]:
     if name in hbm:
         return "hbm", float(hbm[name])
     if name in ("mx_quantize_rows", "mx_quantize_cols"):
-        # per step each quantises X and dY [R, d], A, dHg, dHu [R, f] and the three weights [E, d, f] once
-        # (rows: along the contiguous axis; cols: down the rows, transposed), in 8 launches; per element
-        # the source (s bytes) is read and 1 + 1/32 bytes written
-        elems = 2 * R * d + 3 * R * f + 3 * E * d * f
-        return "hbm", float(elems * (s + 1 + 1 / 32) / 8)
+        # per step each quantises X and dY [R, d] and A, dHg, dHu [R, f] once (rows: along the contiguous
+        # axis; cols: down the rows, transposed, by expert segment), in 5 launches; per element the source
+        # (s bytes) is read and 1 + 1/32 bytes written
+        elems = 2 * R * d + 3 * R * f
+        return "hbm", float(elems * (s + 1 + 1 / 32) / 5)
+    if name == "mx_quantize_both":
+        # one expert weight [E, d, f] per launch (3 per step): read once, written in both layouts
+        return "hbm", float(E * d * f * (s + 2 * (1 + 1 / 32)))
     return "other", 0.0
 
 
@@ -171,6 +174,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: bf16, E=8, top-4)")
     ap.add_argument("--seed", type=int, default=17)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-only", action="store_true",
+                    help="only the warm-up and the timed steps (for profiler traces: every launch belongs to a "
+                         "step), then a short JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--pool-sweep", action="store_true",
                     help="only time the bf16 layer at T=16384, d=2048, k=4, f=1024 for E = 8, 16, 32, 64, 128 "
@@ -229,6 +235,11 @@ def main() -> int:
     stop.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
+    if args.trace_only:
+        print(json.dumps({"metric": METRIC, "value": w.T / (ms_per_step * 1e-3), "unit": "tokens/s",
+                          "ms_per_step": ms_per_step, "steps": args.steps, "warmup": args.warmup,
+                          "workload": w.name, "trace_only": True}), flush=True)
+        return 0
 
     # timed region 2: the same K steps with HIP events around every library launch, recorded on the stream the
     # kernels run on -> per-kernel durations (roofline); the events add their own time to this pass only

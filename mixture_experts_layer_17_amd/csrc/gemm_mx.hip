@@ -363,7 +363,7 @@ int launch_mx_cfg(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
   return launch_status();
 }
 
-bool mx_big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 1024; }
+bool mx_big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 512; }
 bool mx_big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
 
 int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
