@@ -81,12 +81,18 @@ def kernel_work(name: str, w, s: int) -> tuple[str, float]:
         "route_select": 4 * T * E + 12 * R,
         "route_topk_bwd": 8 * R + 4 * T * E + 4 * R,
     }
+    if w.prec == "mxfp8":
+        # the dispatch and the combine backward also write the MX rows layout of x_perm / dy_perm
+        hbm["dispatch"] += R * d * (1 + 1 / 32)
+        hbm["combine_bwd"] += R * d * (1 + 1 / 32)
     if name in hbm:
         return "hbm", float(hbm[name])
-    if name in ("mx_quantize_rows", "mx_quantize_cols"):
-        # per step each quantises X and dY [R, d] and A, dHg, dHu [R, f] once (rows: along the contiguous
-        # axis; cols: down the rows, transposed, by expert segment), in 5 launches; per element the source
-        # (s bytes) is read and 1 + 1/32 bytes written
+    if name == "mx_quantize_rows":
+        # A, dHg, dHu [R, f] along f, one launch each (X and dY come quantised from the dispatch and the combine
+        # backward); per element the source (s bytes) is read and 1 + 1/32 bytes written
+        return "hbm", float(R * f * (s + 1 + 1 / 32))
+    if name == "mx_quantize_cols":
+        # X and dY [R, d], A, dHg, dHu [R, f] down the tokens of each expert segment, transposed: 5 launches
         elems = 2 * R * d + 3 * R * f
         return "hbm", float(elems * (s + 1 + 1 / 32) / 5)
     if name == "mx_quantize_both":

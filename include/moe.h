@@ -149,6 +149,25 @@ int moe_combine_bwd(const void* dout, const void* y_perm, int dtype, const float
                     const int32_t* perm_dst, int64_t T, int32_t d, int32_t k, void* dy_perm,
                     float* dgates, void* stream);
 
+/* MXFP8 data movement ("Scaling and optimizing MoE training": the MXFP8 gains
+ * came from the expert FFN and from moving data between experts): the two
+ * calls that write an expert-major buffer the MXFP8 FFN quantises along d
+ * (X for the gate/up GEMM, dY for the down-projection's data gradient) also
+ * write its MX rows layout, so the FFN skips that quantisation pass.
+ * The MX buffer `*_mx` (caller-owned, moe_mx_act_bytes(R, d) bytes, R = T*k)
+ * holds the E4M3 codes [R, d] (blocks of 32 along d, as mx_quantize axis 1),
+ * then, at the next 256-byte boundary, the E8M0 bytes in grouped order: the
+ * byte of (row r, block b) at ((b/4)*R + r)*4 + b%4.  Codes and scales are
+ * bit-identical to mx_quantize of the bf16 buffer the same call writes.
+ * bf16 only; d % 128 == 0 (else MOE_EUNSUPPORTED); otherwise as moe_dispatch /
+ * moe_combine_bwd.  moe_mx_act_bytes returns 0 for invalid sizes. */
+size_t moe_mx_act_bytes(int64_t rows, int32_t cols);
+int moe_dispatch_mx(const void* x, int64_t T, int32_t d, int32_t k, const int32_t* perm_dst,
+                    void* x_perm, void* x_mx, void* stream);
+int moe_combine_bwd_mx(const void* dout, const void* y_perm, const float* gates, const int32_t* perm_dst,
+                       int64_t T, int32_t d, int32_t k, void* dy_perm, float* dgates, void* dy_mx,
+                       void* stream);
+
 /* ---------------------------------------------------------------------------
  * Grouped SwiGLU expert FFN ("Scaling and optimizing MoE training": the small
  * per-expert products run as one grouped GEMM; MXFP8 where it pays).
@@ -170,17 +189,21 @@ int moe_combine_bwd(const void* dout, const void* y_perm, int dtype, const float
  * mx_wcache (MOE_MXFP8 only, else ignored; may be NULL): a cache built by
  * moe_mx_weight_cache_build from these same weights, E, d and f; with it the
  * call quantises no weight (w_gate/w_up/w_down are still passed and
- * validated); results are bit-identical to those without it. */
+ * validated); results are bit-identical to those without it.
+ * x_mx (forward) / dy_mx (backward) (MOE_MXFP8 only, else MOE_EINVAL; may be
+ * NULL): x_perm / dy_perm already in the MX rows layout written by
+ * moe_dispatch_mx / moe_combine_bwd_mx for the same buffer; the call then does
+ * not quantise it again (bit-identical results). */
 size_t moe_grouped_ffn_workspace(int64_t R, int32_t E, int32_t d, int32_t f, int prec, int is_bwd);
 int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                         const void* x_perm, const void* w_gate, const void* w_up, const void* w_down,
-                        const void* mx_wcache, void* h_gate, void* h_up, void* a_act, void* y_perm,
-                        void* ws, size_t ws_bytes, void* stream);
+                        const void* mx_wcache, const void* x_mx, void* h_gate, void* h_up, void* a_act,
+                        void* y_perm, void* ws, size_t ws_bytes, void* stream);
 int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                         const int32_t* mx_blk_offsets, const void* dy_perm, const void* x_perm,
                         const void* h_gate, const void* h_up, const void* a_act, const void* w_gate,
-                        const void* w_up, const void* w_down, const void* mx_wcache, void* dx_perm,
-                        void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                        const void* w_up, const void* w_down, const void* mx_wcache, const void* dy_mx,
+                        void* dx_perm, void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
                         void* stream);
 
 /* Pre-quantised MXFP8 expert weights ("Scaling and optimizing MoE training":

@@ -39,8 +39,12 @@ _SIGS = {
     "moe_combine_bwd": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
                                _c_void_p, _c_void_p]),
     "moe_grouped_ffn_workspace": (_sz, [_i64, _i32, _i32, _i32, _int, _int]),
-    "moe_grouped_ffn_fwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 10 + [_c_void_p, _sz, _c_void_p]),
-    "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 15 + [_c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_fwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 11 + [_c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 16 + [_c_void_p, _sz, _c_void_p]),
+    "moe_mx_act_bytes": (_sz, [_i64, _i32]),
+    "moe_dispatch_mx": (_int, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_combine_bwd_mx": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
+                                  _c_void_p, _c_void_p, _c_void_p]),
     "moe_mx_weight_cache_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_stats": (_int, [_c_void_p, _i32, _c_void_p, _c_void_p]),
     "moe_mx_weight_cache_build": (_int, [_c_void_p] * 3 + [_i32, _i32, _i32, _c_void_p, _sz, _c_void_p]),
@@ -164,6 +168,29 @@ def moe_dispatch(x, perm_dst, k, out=None):
     return out
 
 
+def moe_mx_act_buffer(rows, cols, device):
+    """Caller buffer for moe_dispatch_mx / moe_combine_bwd_mx: E4M3 codes [rows, cols], then grouped scales."""
+    n = lib().moe_mx_act_bytes(rows, cols)
+    if n == 0:
+        raise MoeError(f"moe_mx_act_bytes({rows}, {cols}): unsupported size")
+    return _ws(n, device)
+
+
+def mx_act_split(buf, rows, cols):
+    """(codes uint8 [rows, cols], grouped scale bytes uint8 [rows * cols / 32]) views of an MX activation buffer."""
+    off = -(-rows * cols // 256) * 256
+    return buf[:rows * cols].view(rows, cols), buf[off:off + rows * cols // 32]
+
+
+def moe_dispatch_mx(x, perm_dst, k, out=None, mx=None):
+    """moe_dispatch that also writes the MX rows layout of x_perm (bf16, d % 128 == 0); returns (x_perm, mx)."""
+    T, d = x.shape
+    out = torch.empty((T * k, d), dtype=x.dtype, device=x.device) if out is None else out
+    mx = moe_mx_act_buffer(T * k, d, x.device) if mx is None else mx
+    _check(lib().moe_dispatch_mx(_p(x), T, d, k, _p(perm_dst), _p(out), _p(mx), _stream()), "moe_dispatch_mx")
+    return out, mx
+
+
 def moe_dispatch_bwd(dx_perm, perm_dst, k, out=None):
     R, d = dx_perm.shape
     T = R // k
@@ -192,6 +219,18 @@ def moe_combine_bwd(dout, y_perm, gates, perm_dst, dy_perm=None, dgates=None):
     return dy_perm, dgates
 
 
+def moe_combine_bwd_mx(dout, y_perm, gates, perm_dst, dy_perm=None, dgates=None, mx=None):
+    """moe_combine_bwd that also writes the MX rows layout of dy_perm; returns (dy_perm, dgates, mx)."""
+    T, k = gates.shape
+    d = dout.shape[1]
+    dy_perm = torch.empty_like(y_perm) if dy_perm is None else dy_perm
+    dgates = torch.empty((T, k), dtype=torch.float32, device=dout.device) if dgates is None else dgates
+    mx = moe_mx_act_buffer(T * k, d, dout.device) if mx is None else mx
+    _check(lib().moe_combine_bwd_mx(_p(dout), _p(y_perm), _p(gates), _p(perm_dst), T, d, k, _p(dy_perm), _p(dgates),
+                                    _p(mx), _stream()), "moe_combine_bwd_mx")
+    return dy_perm, dgates, mx
+
+
 def moe_route_stats(counts, out=None):
     """counts [E] int32 (device) -> int32 [4] on the device: max rows, min rows, empty experts, total rows."""
     E = counts.shape[0]
@@ -206,7 +245,7 @@ def moe_grouped_ffn_workspace(R, E, d, f, prec, is_bwd):
     return lib().moe_grouped_ffn_workspace(R, E, d, f, _PREC[prec], int(is_bwd))
 
 
-def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, ws=None, mx_wcache=None):
+def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, ws=None, mx_wcache=None, x_mx=None):
     R, d = x_perm.shape
     E, _, f = w_gate.shape
     dev = x_perm.device
@@ -215,14 +254,14 @@ def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, w
         out["y_perm"] = torch.empty((R, d), dtype=x_perm.dtype, device=dev)
     ws = _ws(moe_grouped_ffn_workspace(R, E, d, f, prec, 0), dev) if ws is None else ws
     _check(lib().moe_grouped_ffn_fwd(R, E, d, f, _PREC[prec], _p(offsets), _p(x_perm), _p(w_gate), _p(w_up),
-                                     _p(w_down), _p(mx_wcache), _p(out["h_gate"]), _p(out["h_up"]),
+                                     _p(w_down), _p(mx_wcache), _p(x_mx), _p(out["h_gate"]), _p(out["h_up"]),
                                      _p(out["a_act"]), _p(out["y_perm"]), _p(ws), ws.numel(), _stream()),
            "moe_grouped_ffn_fwd")
     return out
 
 
 def moe_grouped_ffn_bwd(dy_perm, x_perm, h_gate, h_up, a_act, offsets, mx_blk_offsets, w_gate, w_up, w_down, prec,
-                        out=None, ws=None, mx_wcache=None):
+                        out=None, ws=None, mx_wcache=None, dy_mx=None):
     R, d = x_perm.shape
     E, _, f = w_gate.shape
     dev = x_perm.device
@@ -232,7 +271,7 @@ def moe_grouped_ffn_bwd(dy_perm, x_perm, h_gate, h_up, a_act, offsets, mx_blk_of
     ws = _ws(moe_grouped_ffn_workspace(R, E, d, f, prec, 1), dev) if ws is None else ws
     _check(lib().moe_grouped_ffn_bwd(R, E, d, f, _PREC[prec], _p(offsets), _p(mx_blk_offsets), _p(dy_perm),
                                      _p(x_perm), _p(h_gate), _p(h_up), _p(a_act), _p(w_gate), _p(w_up), _p(w_down),
-                                     _p(mx_wcache), _p(out["dx_perm"]), _p(out["dw_gate"]), _p(out["dw_up"]),
+                                     _p(mx_wcache), _p(dy_mx), _p(out["dx_perm"]), _p(out["dw_gate"]), _p(out["dw_up"]),
                                      _p(out["dw_down"]), _p(ws), ws.numel(), _stream()), "moe_grouped_ffn_bwd")
     return out
 

@@ -127,7 +127,7 @@ void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t m
 
 using namespace moe;
 
-extern "C" int moe_abi_version(void) { return 2; }
+extern "C" int moe_abi_version(void) { return 3; }
 
 extern "C" const char* moe_status_str(int status) {
   switch (status) {
@@ -165,16 +165,17 @@ extern "C" int moe_mx_weight_cache_build(const void* w_gate, const void* w_up, c
 
 extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                                    const void* x_perm, const void* w_gate, const void* w_up, const void* w_down,
-                                   const void* mx_wcache, void* h_gate, void* h_up, void* a_act, void* y_perm,
-                                   void* ws, size_t ws_bytes, void* stream) {
+                                   const void* mx_wcache, const void* x_mx, void* h_gate, void* h_up, void* a_act,
+                                   void* y_perm, void* ws, size_t ws_bytes, void* stream) {
   const FfnShape sh{R, E, d, f, prec};
   if (!shape_ok(sh)) return MOE_EINVAL;
   if (!shape_supported(sh)) return MOE_EUNSUPPORTED;
   if (!offsets || !w_gate || !w_up || !w_down || !ws) return MOE_EINVAL;
   if (R > 0 && (!x_perm || !h_gate || !h_up || !a_act || !y_perm)) return MOE_EINVAL;
-  for (const void* p : {x_perm, w_gate, w_up, w_down, mx_wcache, (const void*)h_gate, (const void*)h_up,
+  for (const void* p : {x_perm, w_gate, w_up, w_down, mx_wcache, x_mx, (const void*)h_gate, (const void*)h_up,
                         (const void*)a_act, (const void*)y_perm, (const void*)ws})
     if (p && !aligned16(p)) return MOE_EINVAL;
+  if (x_mx && prec != MOE_MXFP8) return MOE_EINVAL;
   if (ws_bytes < ffn_ws_bytes(sh, 0)) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (R == 0) return MOE_OK;
@@ -192,7 +193,7 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.o_hg = h_gate; a.o_hu = h_up; a.o_act = a_act; a.act = a_act; a.o_y = y_perm;
   if (prec == MOE_MXFP8) {
     char* mxs = static_cast<char*>(ws) + tiles_bytes(sh);
-    return mx_ffn_fwd(a, mt, static_cast<const char*>(mx_wcache), mxs, s);
+    return mx_ffn_fwd(a, mt, static_cast<const char*>(mx_wcache), static_cast<const uint8_t*>(x_mx), mxs, s);
   }
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
   int st = launch(kG1, a, mt, s);
@@ -203,19 +204,20 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
 extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                                    const int32_t* mx_blk_offsets, const void* dy_perm, const void* x_perm,
                                    const void* h_gate, const void* h_up, const void* a_act, const void* w_gate,
-                                   const void* w_up, const void* w_down, const void* mx_wcache, void* dx_perm,
-                                   void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   const void* w_up, const void* w_down, const void* mx_wcache, const void* dy_mx,
+                                   void* dx_perm, void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                                   size_t ws_bytes, void* stream) {
   const FfnShape sh{R, E, d, f, prec};
   if (!shape_ok(sh)) return MOE_EINVAL;
   if (!shape_supported(sh)) return MOE_EUNSUPPORTED;
   if (!offsets || !w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down || !ws) return MOE_EINVAL;
   if (R > 0 && (!dy_perm || !x_perm || !h_gate || !h_up || !a_act || !dx_perm)) return MOE_EINVAL;
   if (prec == MOE_MXFP8 && !mx_blk_offsets) return MOE_EINVAL;
-  for (const void* p : {dy_perm, x_perm, h_gate, h_up, a_act, w_gate, w_up, w_down, mx_wcache,
+  for (const void* p : {dy_perm, x_perm, h_gate, h_up, a_act, w_gate, w_up, w_down, mx_wcache, dy_mx,
                         (const void*)dx_perm, (const void*)dw_gate, (const void*)dw_up, (const void*)dw_down,
                         (const void*)ws})
     if (p && !aligned16(p)) return MOE_EINVAL;
+  if (dy_mx && prec != MOE_MXFP8) return MOE_EINVAL;
   if (ws_bytes < ffn_ws_bytes(sh, 1)) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bm = tile_bm(prec, R, E);
@@ -238,7 +240,8 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.o_dx = dx_perm; a.o_dwg = dw_gate; a.o_dwu = dw_up; a.o_dwd = dw_down;
   if (prec == MOE_MXFP8) {
     char* mxs = wsb + tiles_bytes(sh) + 2 * hbytes;
-    return mx_ffn_bwd(a, mt, mx_blk_offsets, static_cast<const char*>(mx_wcache), mxs, s);
+    return mx_ffn_bwd(a, mt, mx_blk_offsets, static_cast<const char*>(mx_wcache), static_cast<const uint8_t*>(dy_mx),
+                      mxs, s);
   }
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
   int st = MOE_OK;

@@ -487,14 +487,15 @@ size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd) {
   return c.used;
 }
 
-int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* scratch, hipStream_t s) {
+int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, const uint8_t* x_mx, char* scratch,
+               hipStream_t s) {
   Carve c{scratch};
   const FwdBufs b = carve_fwd(c, a.R, a.E, a.d, a.f);
   const int bf = MOE_BF16;
   MxArgs m{};
   m.f = a;
   // X along d (rows); Wg, Wu [E][d][f] along d -> [E][f][d]; Wd [E][f][d] along f -> [E][d][f]
-  launch_mx_rows(a.x, bf, a.R, a.d, b.x.q, b.x.s, s, true);
+  if (!x_mx) launch_mx_rows(a.x, bf, a.R, a.d, b.x.q, b.x.s, s, true);
   if (wcache) {
     Carve cc{const_cast<char*>(wcache)};
     const WCache w = carve_wcache(cc, a.E, a.d, a.f);
@@ -505,7 +506,8 @@ int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* sc
     launch_mx_cols(a.wd, bf, a.E, a.f, a.d, nullptr, 0, a.f, b.wd.q, b.wd.s, s, true, nullptr);
     m.wgq = b.wg.q; m.wgs = b.wg.s; m.wuq = b.wu.q; m.wus = b.wu.s; m.wdq = b.wd.q; m.wds = b.wd.s;
   }
-  m.xq = b.x.q; m.xs = b.x.s;
+  m.xq = x_mx ? x_mx : b.x.q;
+  m.xs = x_mx ? x_mx + align_up(static_cast<size_t>(a.R) * a.d, 256) : b.x.s;
   int st = launch_mx_kind(kG1, m, max_tiles, s);
   if (st != MOE_OK) return st;
   launch_mx_rows(a.o_act, bf, a.R, a.f, b.a.q, b.a.s, s, true);
@@ -513,8 +515,8 @@ int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* sc
   return launch_mx_kind(kG2, m, max_tiles, s);
 }
 
-int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache, char* scratch,
-               hipStream_t s) {
+int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache,
+               const uint8_t* dy_mx, char* scratch, hipStream_t s) {
   Carve c{scratch};
   const BwdBufs b = carve_bwd(c, a.R, a.E, a.d, a.f);
   const int bf = MOE_BF16;
@@ -535,8 +537,9 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
       m.wdq = b.wd.q; m.wds = b.wd.s;
     }
     // G3: dA = dY Wd^T: dY along d, Wd natural [E][f][d] along d
-    launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s, true);
-    m.dyq = b.dy.q; m.dys = b.dy.s;
+    if (!dy_mx) launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s, true);
+    m.dyq = dy_mx ? dy_mx : b.dy.q;
+    m.dys = dy_mx ? dy_mx + align_up(static_cast<size_t>(a.R) * a.d, 256) : b.dy.s;
     st = launch_mx_kind(kG3, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f

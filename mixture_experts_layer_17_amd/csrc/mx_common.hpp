@@ -70,10 +70,13 @@ void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows,
 // MXFP8 expert FFN (gemm_mx.hip).
 size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd);
 int ffn_mx_bm(int64_t R, int E);  // row-tile height for this workload
-//  wcache: NULL, or a weight cache built by mx_wcache_build for the same weights (then no weight is quantised)
-int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, char* scratch, hipStream_t s);
-int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache, char* scratch,
+//  wcache: NULL, or a weight cache built by mx_wcache_build for the same weights (then no weight is quantised).
+//  x_mx / dy_mx: NULL, or X / dY already in the MX rows layout (codes [R, d], then at the next 256-byte boundary
+//  the grouped scale words), as moe_dispatch_mx / moe_combine_bwd_mx write them.
+int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, const uint8_t* x_mx, char* scratch,
                hipStream_t s);
+int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache,
+               const uint8_t* dy_mx, char* scratch, hipStream_t s);
 size_t mx_wcache_bytes(int E, int d, int f);
 void mx_wcache_build(const void* wg, const void* wu, const void* wd, int E, int d, int f, char* cache,
                      hipStream_t s);

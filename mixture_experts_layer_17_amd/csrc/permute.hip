@@ -11,7 +11,7 @@
 // whole 16-byte-vector rows.  Every access is a 16-byte vector, 1 KiB per wave
 // instruction.  The k row indices of a token are wave-uniform scalar loads.
 // Sums run in fp32 in slot order j = 0..k-1.
-#include "common.hpp"
+#include "mx_common.hpp"
 
 namespace moe {
 namespace {
@@ -140,6 +140,141 @@ __global__ __launch_bounds__(64 * kWaves) void combine_bwd_kernel(const T* __res
   }
 }
 
+// MX rows layout of one expert-buffer row segment, computed where the row is
+// written (Olmo-core 3 announcement, "Scaling and optimizing MoE training":
+// MXFP8 gains come from the expert FFN and from moving data between experts).
+// Lane l holds 16-byte vector c (8 bf16 values, c = 64 i + l) of the row: four
+// lanes form a 32-element block (amax over two lane exchanges), sixteen a group
+// of four blocks whose E8M0 bytes make one 32-bit word (two more exchanges).
+// Returns the 8 E4M3 codes; *word is the group's scale word (valid in every lane).
+__device__ __forceinline__ uint2 mx_encode8(const float* v, uint32_t* word, int c) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int e = mx_block_exponent(amax);
+  const float inv = mx_inv_scale(e);
+  uint32_t sw = static_cast<uint32_t>(e + 127) << (8 * ((c >> 2) & 3));
+  sw |= __shfl_xor(sw, 4, 64);
+  sw |= __shfl_xor(sw, 8, 64);
+  *word = sw;
+  return make_uint2(e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                    e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
+}
+
+// Dispatch that also writes the MX rows layout of every expert row: codes
+// q[row * d + col], scale word of (row, group G) at sw[G * R + row].  bf16,
+// d % 128 == 0 (a group never straddles lanes of different waves).
+__global__ __launch_bounds__(64 * kWaves) void dispatch_mx_kernel(const uint16_t* __restrict__ x, int64_t Tn, int d,
+                                                                 int k, const int32_t* __restrict__ perm_dst,
+                                                                 uint16_t* __restrict__ x_perm,
+                                                                 uint8_t* __restrict__ q, uint32_t* __restrict__ sw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int64_t R = Tn * k;
+  const int nvec = d / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+  int rows[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) rows[j] = j < k ? perm_dst[t * k + j] : 0;
+  for (int c0 = 0; c0 < nvec; c0 += 64 * kMaxChunks) {
+    uint4 v[kMaxChunks];
+    uint2 cq[kMaxChunks];
+    uint32_t cw[kMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = c0 + i * 64 + lane;
+      if (c0 + i * 64 < nvec) {  // wave-uniform: whole groups of 16 lanes are valid together
+        v[i] = c < nvec ? src[c] : make_uint4(0, 0, 0, 0);
+        float f[8];
+        Elem<uint16_t>::unpack(v[i], f);
+        cq[i] = mx_encode8(f, &cw[i], c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int64_t row = rows[j];
+      uint4* dst = reinterpret_cast<uint4*>(x_perm + row * d);
+      uint2* dq = reinterpret_cast<uint2*>(q + row * d);
+#pragma unroll
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = c0 + i * 64 + lane;
+        if (c < nvec) {
+          store16_nt(dst + c, v[i]);
+          dq[c] = cq[i];
+          if ((c & 15) == 0) sw[static_cast<int64_t>(c >> 4) * R + row] = cw[i];
+        }
+      }
+    }
+  }
+}
+
+// combine_bwd that also writes the MX rows layout of dy_perm (codes and scale
+// words as in dispatch_mx_kernel), encoded from the stored bf16 values.
+// bf16, d % 128 == 0.
+__global__ __launch_bounds__(64 * kWaves) void combine_bwd_mx_kernel(
+    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y_perm, int64_t Tn, int d, int k,
+    const int32_t* __restrict__ perm_dst, const float* __restrict__ gates, uint16_t* __restrict__ dy_perm,
+    float* __restrict__ dgates, uint8_t* __restrict__ q, uint32_t* __restrict__ sw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int64_t R = Tn * k;
+  const int nvec = d / 8;
+  int rows[kMaxK];
+  float g[kMaxK], dot[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rows[j] = j < k ? perm_dst[t * k + j] : 0;
+    g[j] = j < k ? gates[t * k + j] : 0.f;
+    dot[j] = 0.f;
+  }
+  const uint4* src = reinterpret_cast<const uint4*>(dout + t * d);
+  for (int c0 = 0; c0 < nvec; c0 += 64) {  // wave-uniform trip count; groups of 16 lanes are valid together
+    const int c = c0 + lane;
+    const bool ok = c < nvec;
+    float o[8];
+    Elem<uint16_t>::unpack(ok ? src[c] : make_uint4(0, 0, 0, 0), o);
+    uint4 yv[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) yv[j] = ok ? reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[c]
+                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        float y[8], sv[8];
+        Elem<uint16_t>::unpack(yv[j], y);
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { p += o[i] * y[i]; sv[i] = g[j] * o[i]; }
+        dot[j] += p;
+        const uint4 packed = Elem<uint16_t>::pack(sv);
+        float r[8];
+        Elem<uint16_t>::unpack(packed, r);  // quantise the stored (bf16) values
+        uint32_t word;
+        const uint2 cq = mx_encode8(r, &word, c);
+        if (ok) {
+          const int64_t row = rows[j];
+          reinterpret_cast<uint4*>(dy_perm + row * d)[c] = packed;
+          reinterpret_cast<uint2*>(q + row * d)[c] = cq;
+          if ((c & 15) == 0) sw[static_cast<int64_t>(c >> 4) * R + row] = word;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      const float s = wave_sum(dot[j]);
+      if (lane == 0) dgates[t * k + j] = s;
+    }
+  }
+}
+
 bool dims_ok(int dtype, int64_t T, int d, int k) {
   return (dtype == MOE_F32 || dtype == MOE_BF16) && T >= 0 && d > 0 && d % 8 == 0 && k >= 1 && k <= kMaxK &&
          T * k < (1ll << 31) && static_cast<int64_t>(d) * (T * k) < (1ll << 62);
@@ -164,6 +299,45 @@ extern "C" int moe_dispatch(const void* x, int dtype, int64_t T, int32_t d, int3
   else
     MOE_LAUNCH("dispatch", dispatch_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
                        static_cast<const uint16_t*>(x), T, d, k, perm_dst, static_cast<uint16_t*>(x_perm));
+  return launch_status();
+}
+
+extern "C" size_t moe_mx_act_bytes(int64_t rows, int32_t cols) {
+  if (rows < 0 || cols <= 0 || cols % 128) return 0;
+  return align_up(static_cast<size_t>(rows) * cols, 256) + static_cast<size_t>(rows) * (cols / 32);
+}
+
+extern "C" int moe_dispatch_mx(const void* x, int64_t T, int32_t d, int32_t k, const int32_t* perm_dst,
+                               void* x_perm, void* x_mx, void* stream) {
+  if (!dims_ok(MOE_BF16, T, d, k)) return MOE_EINVAL;
+  if (d % 128) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !perm_dst || !x_perm || !x_mx || !aligned16(x) || !aligned16(x_perm) || !aligned16(x_mx))
+    return MOE_EINVAL;
+  const int64_t R = T * k;
+  uint8_t* q = static_cast<uint8_t*>(x_mx);
+  uint32_t* sw = reinterpret_cast<uint32_t*>(q + align_up(static_cast<size_t>(R) * d, 256));
+  MOE_LAUNCH("dispatch", dispatch_mx_kernel, grid_for(T), dim3(64 * kWaves), 0, static_cast<hipStream_t>(stream),
+             static_cast<const uint16_t*>(x), T, d, k, perm_dst, static_cast<uint16_t*>(x_perm), q, sw);
+  return launch_status();
+}
+
+extern "C" int moe_combine_bwd_mx(const void* dout, const void* y_perm, const float* gates, const int32_t* perm_dst,
+                                  int64_t T, int32_t d, int32_t k, void* dy_perm, float* dgates, void* dy_mx,
+                                  void* stream) {
+  if (!dims_ok(MOE_BF16, T, d, k)) return MOE_EINVAL;
+  if (d % 128) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!dout || !y_perm || !gates || !perm_dst || !dy_perm || !dgates || !dy_mx || !aligned16(dout) ||
+      !aligned16(y_perm) || !aligned16(dy_perm) || !aligned16(dy_mx))
+    return MOE_EINVAL;
+  const int64_t R = T * k;
+  uint8_t* q = static_cast<uint8_t*>(dy_mx);
+  uint32_t* sw = reinterpret_cast<uint32_t*>(q + align_up(static_cast<size_t>(R) * d, 256));
+  MOE_LAUNCH("combine_bwd", combine_bwd_mx_kernel, grid_for(T), dim3(64 * kWaves), 0,
+             static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(dout),
+             static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst, gates, static_cast<uint16_t*>(dy_perm), dgates,
+             q, sw);
   return launch_status();
 }
 

@@ -38,14 +38,18 @@ class LayerStep:
                             (moe_mx_weight_cache_build), and its forward and backward use them: the weights
                             change once per optimiser step, so this is the whole per-step conversion;
       mx_weight_cache       quantised once here and reused by every step (valid while the weights do not change).
+    MXFP8 activations: with mx_fused_movement (the default) the dispatch and the combine backward also write the
+    MX rows layout of x_perm and dy_perm (moe_dispatch_mx / moe_combine_bwd_mx), which the FFN then uses instead
+    of quantising those buffers again; bit-identical results either way.
     """
 
     def __init__(self, w: Workload, dev_inputs: dict, mx_weight_cache: bool = False,
-                 mx_weights_per_step: bool = False):
+                 mx_weights_per_step: bool = False, mx_fused_movement: bool = True):
         self.w = w
         self.inp = dev_inputs
         self.mx_wcache = None
         self.mx_per_step = bool(mx_weights_per_step) and w.prec == "mxfp8"
+        self.mx_fused = bool(mx_fused_movement) and w.prec == "mxfp8"
         x = dev_inputs["x"]
         dev = x.device
         T, d, E, k, f, R = w.T, w.d, w.E, w.k, w.f, w.R
@@ -65,6 +69,8 @@ class LayerStep:
         }
         self.route_ws = B._ws(B.lib().moe_route_topk_workspace(T, E, k), dev)
         self.x_perm = torch.empty((R, d), dtype=dt, device=dev)
+        self.x_mx = B.moe_mx_act_buffer(R, d, dev) if self.mx_fused else None
+        self.dy_mx = B.moe_mx_act_buffer(R, d, dev) if self.mx_fused else None
         self.ffn = {n: torch.empty((R, f), dtype=dt, device=dev) for n in ("h_gate", "h_up", "a_act")}
         self.ffn["y_perm"] = torch.empty((R, d), dtype=dt, device=dev)
         self.ffn_ws_f = B._ws(B.moe_grouped_ffn_workspace(R, E, d, f, w.prec, 0), dev)
@@ -98,20 +104,28 @@ class LayerStep:
         if self.linear_router:
             B.moe_router_logits(inp["x"], inp["w_router"], out=self.logits)
         B.moe_route_topk(self.logits, w.k, out=self.route, ws=self.route_ws)
-        B.moe_dispatch(inp["x"], self.route["perm_dst"], w.k, out=self.x_perm)
+        if self.mx_fused:
+            B.moe_dispatch_mx(inp["x"], self.route["perm_dst"], w.k, out=self.x_perm, mx=self.x_mx)
+        else:
+            B.moe_dispatch(inp["x"], self.route["perm_dst"], w.k, out=self.x_perm)
         B.moe_grouped_ffn_fwd(self.x_perm, self.route["offsets"], inp["w_gate"], inp["w_up"], inp["w_down"], w.prec,
-                              out=self.ffn, ws=self.ffn_ws_f, mx_wcache=self.mx_wcache)
+                              out=self.ffn, ws=self.ffn_ws_f, mx_wcache=self.mx_wcache, x_mx=self.x_mx)
         B.moe_combine(self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"], out=self.out)
         return self.out
 
     def backward(self, dout=None):
         w, inp = self.w, self.inp
         dout = inp["dout"] if dout is None else dout
-        B.moe_combine_bwd(dout, self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"],
-                          dy_perm=self.dy_perm, dgates=self.dgates)
+        if self.mx_fused:
+            B.moe_combine_bwd_mx(dout, self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"],
+                                 dy_perm=self.dy_perm, dgates=self.dgates, mx=self.dy_mx)
+        else:
+            B.moe_combine_bwd(dout, self.ffn["y_perm"], self.route["gates"], self.route["perm_dst"],
+                              dy_perm=self.dy_perm, dgates=self.dgates)
         B.moe_grouped_ffn_bwd(self.dy_perm, self.x_perm, self.ffn["h_gate"], self.ffn["h_up"], self.ffn["a_act"],
                               self.route["offsets"], self.route["mx_blk_offsets"], inp["w_gate"], inp["w_up"],
-                              inp["w_down"], w.prec, out=self.grads, ws=self.ffn_ws_b, mx_wcache=self.mx_wcache)
+                              inp["w_down"], w.prec, out=self.grads, ws=self.ffn_ws_b, mx_wcache=self.mx_wcache,
+                              dy_mx=self.dy_mx)
         B.moe_dispatch_bwd(self.grads["dx_perm"], self.route["perm_dst"], w.k, out=self.dx)
         B.moe_route_topk_bwd(self.route["gates"], self.dgates, self.route["topk_idx"], w.E, out=self.dlogits)
         if self.linear_router:

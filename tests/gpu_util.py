@@ -52,9 +52,10 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def run_gpu_step(w: wl.Workload, inp: dict, mx_weight_cache: bool = False,
-                 mx_weights_per_step: bool = False) -> tuple[dict, L.LayerStep]:
-    step = L.LayerStep(w, L.to_device(inp), mx_weight_cache=mx_weight_cache, mx_weights_per_step=mx_weights_per_step)
+def run_gpu_step(w: wl.Workload, inp: dict, mx_weight_cache: bool = False, mx_weights_per_step: bool = False,
+                 mx_fused_movement: bool = True) -> tuple[dict, L.LayerStep]:
+    step = L.LayerStep(w, L.to_device(inp), mx_weight_cache=mx_weight_cache, mx_weights_per_step=mx_weights_per_step,
+                       mx_fused_movement=mx_fused_movement)
     step.step()
     torch.cuda.synchronize()
     res = {k: host(v) for k, v in step.route.items()}

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert L.moe_status_str(0) == b"ok"
     assert L.moe_status_str(3) == b"workspace too small"
 
@@ -63,18 +63,35 @@ def test_route_topk_validation(L):
 
 def test_ffn_validation(L):
     s = None
-    args = [FAKE] * 10
+    args = [FAKE] * 11
+    no_xmx = [FAKE] * 6 + [None] + [FAKE] * 4   # x_mx NULL
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1000, 1, *args, FAKE, 1 << 30, s) == EUNSUP   # f % 64
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 7, *args, FAKE, 1 << 30, s) == EINVAL   # bad precision
-    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *args, FAKE, 16, s) == EWS
-    bargs = [FAKE] * 15
-    assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *bargs, FAKE, 16, s) == EWS
-    bargs_nomx = [FAKE, None] + [FAKE] * 13
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *no_xmx, FAKE, 16, s) == EWS
+    bargs = [FAKE] * 16
+    no_dymx = [FAKE] * 11 + [None] + [FAKE] * 4  # dy_mx NULL
+    assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *no_dymx, FAKE, 16, s) == EWS
+    bargs_nomx = [FAKE, None] + [FAKE] * 14
     assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 2, *bargs_nomx, FAKE, 1 << 40, s) == EINVAL
-    unaligned = [FAKE] + [ctypes.c_void_p(0x10008)] + [FAKE] * 8
+    unaligned = [FAKE] + [ctypes.c_void_p(0x10008)] + [FAKE] * 4 + [None] + [FAKE] * 4
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *unaligned, FAKE, 1 << 30, s) == EINVAL
-    bad_cache = [FAKE] * 5 + [ctypes.c_void_p(0x10004)] + [FAKE] * 4        # unaligned weight cache
+    bad_cache = [FAKE] * 5 + [ctypes.c_void_p(0x10004)] + [FAKE] * 5        # unaligned weight cache
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 2, *bad_cache, FAKE, 1 << 40, s) == EINVAL
+    # pre-quantised activations: MXFP8 only
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *args, FAKE, 1 << 40, s) == EINVAL   # x_mx with bf16
+    assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *bargs, FAKE, 1 << 40, s) == EINVAL  # dy_mx with bf16
+
+
+def test_mx_data_movement_validation(L):
+    s = None
+    assert L.moe_mx_act_bytes(1000, 256) == ((1000 * 256 + 255) // 256) * 256 + 1000 * 256 // 32
+    assert L.moe_mx_act_bytes(1000, 200) == 0 and L.moe_mx_act_bytes(-1, 256) == 0
+    assert L.moe_dispatch_mx(FAKE, 10, 200, 2, FAKE, FAKE, FAKE, s) == EUNSUP              # d % 128
+    assert L.moe_dispatch_mx(FAKE, 10, 256, 9, FAKE, FAKE, FAKE, s) == EINVAL              # k > 8
+    assert L.moe_dispatch_mx(FAKE, 10, 256, 2, FAKE, FAKE, None, s) == EINVAL              # null MX buffer
+    assert L.moe_dispatch_mx(FAKE, 0, 256, 2, None, None, None, s) == 0                    # nothing to do
+    assert L.moe_combine_bwd_mx(FAKE, FAKE, FAKE, FAKE, 10, 192, 2, FAKE, FAKE, FAKE, s) == EUNSUP
+    assert L.moe_combine_bwd_mx(FAKE, FAKE, FAKE, FAKE, 10, 256, 2, FAKE, FAKE, ctypes.c_void_p(0x10004), s) == EINVAL
 
 
 def test_route_stats_validation(L):

@@ -116,6 +116,48 @@ def test_dispatch_combine_and_backward(gpu, dtype, T, d, E, k):
     assert gu.rel_err(gu.host(dx), mo.dispatch_backward(yf, meta["perm_dst"], k)) <= tol
 
 
+def _mx_act_host(buf, R, d):
+    """MX activation buffer -> (codes [R, d], scales [R, d/32] in the public row-major order)."""
+    q, sg = B.mx_act_split(buf, R, d)
+    q, sg = q.cpu().numpy(), sg.cpu().numpy()
+    r = np.arange(R)[:, None]
+    b = np.arange(d // 32)[None, :]
+    return q, sg[((b // 4) * R + r) * 4 + b % 4]  # grouped byte of (row r, block b)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(333, 256, 8, 2), (1000, 2048, 128, 4), (77, 4096, 16, 8), (5, 128, 4, 1)])
+def test_dispatch_and_combine_bwd_mx_bit_exact(gpu, T, d, E, k):
+    """The MX-writing dispatch and combine backward: bf16 outputs identical to the plain calls, E4M3 codes and
+    E8M0 scales identical to the oracle's quantiser applied to those bf16 rows."""
+    gu.say(f"case permute MX T={T} d={d} E={E} k={k}")
+    r = np.random.default_rng(7 + T + d)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    idx = mo.topk_select(lg, k)
+    meta = mo.routing_metadata(idx, E)
+    g = mo.topk_gates(lg, idx).astype(np.float32)
+    scale = np.exp2(r.integers(-20, 20, (T, 1))).astype(np.float32)  # a spread of block exponents
+    x = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32) * scale).to(torch.bfloat16)
+    y = torch.randn((T * k, d), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    dout = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32) * scale).to(torch.bfloat16)
+    pd = torch.from_numpy(meta["perm_dst"]).cuda()
+    gd = torch.from_numpy(g).cuda()
+    xd, yd, dd = x.cuda(), y.cuda(), dout.cuda()
+    xp_ref = B.moe_dispatch(xd, pd, k)
+    dy_ref, dg_ref = B.moe_combine_bwd(dd, yd, gd, pd)
+    xp, xmx = B.moe_dispatch_mx(xd, pd, k)
+    dy, dg, dymx = B.moe_combine_bwd_mx(dd, yd, gd, pd)
+    torch.cuda.synchronize()
+    R = T * k
+    np.testing.assert_array_equal(gu.host(xp), gu.host(xp_ref))
+    np.testing.assert_array_equal(gu.host(dy), gu.host(dy_ref))
+    np.testing.assert_array_equal(dg.cpu().numpy(), dg_ref.cpu().numpy())
+    for buf, rows in ((xmx, xp), (dymx, dy)):
+        q, sc = _mx_act_host(buf, R, d)
+        rq, rs = mxo.mx_quantize(rows.float().cpu().numpy().astype(np.float64), axis=1)
+        np.testing.assert_array_equal(q, rq)
+        np.testing.assert_array_equal(sc, rs)
+
+
 # (T, d, E, accumulate): E <= 8 and E <= 16 take the LDS-staged kernels (d not a
 # multiple of 512 leaves a partly filled feature group), E = 24 the generic ones
 ROUTER_CASES = [(700, 256, 8, True), (1000, 520, 6, False), (333, 1024, 16, True), (300, 264, 24, True),

@@ -65,6 +65,20 @@ def test_layer_deterministic(gpu):
 
 
 @pytest.mark.parametrize("name", ["mxfp8-e16", "mxfp8-big-tiles"])
+def test_mx_fused_movement_bit_identical(gpu, name):
+    """Quantising x_perm and dy_perm inside the dispatch and the combine backward (moe_dispatch_mx,
+    moe_combine_bwd_mx) gives the same bits as letting the FFN quantise them."""
+    w = SMALL[name]
+    gu.say(f"case fused MX movement {name}")
+    inp = wl.make_inputs(w)
+    a, step_a = gu.run_gpu_step(w, inp, mx_fused_movement=False)
+    b, step_b = gu.run_gpu_step(w, inp, mx_fused_movement=True)
+    assert step_a.x_mx is None and step_b.x_mx is not None
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["mxfp8-e16", "mxfp8-big-tiles"])
 def test_mx_weight_cache_bit_identical(gpu, name):
     """A step on pre-quantised weights (moe_mx_weight_cache_build) gives the same bits as one that quantises
     the weights itself."""
