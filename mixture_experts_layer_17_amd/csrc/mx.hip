@@ -232,15 +232,18 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     if (c0 + oc < cols && b0 + j < nblk) sb[(c0 + oc) * (ldq / 32) + b0 + j] = osc[oc][j];
   }
   if constexpr (BOTH) {
-    // row layout: tile row tr = tid / 2, column block cb = tid % 2 (32 elements)
-    const int tr = tid >> 1, cb = tid & 1;
-    const int64_t r = b0 * 32 + tr;
-    const int64_t cc = c0 + cb * 32;
-    if (r < rows && cc < cols) {
-      float v[32];
-      const T* tp = tile + tr * LDT + cb * 32;
+    // row layout: in each half of the tile, four lanes per tile row (16
+    // columns each, two lanes per 32-element block), so that a store
+    // instruction writes 16 whole 64-byte row segments
+    const int qt = tid & 3;
 #pragma unroll
-      for (int u = 0; u < 32 / VEC; ++u) {
+    for (int h = 0; h < 2; ++h) {
+      const int tr = h * 64 + (tid >> 2);
+      const int64_t r = b0 * 32 + tr;
+      float v[16];
+      const T* tp = tile + tr * LDT + qt * 16;
+#pragma unroll
+      for (int u = 0; u < 16 / VEC; ++u) {
         const uint4 raw = *reinterpret_cast<const uint4*>(tp + u * VEC);
         float tmp[VEC];
         Elem<T>::unpack(raw, tmp);
@@ -249,17 +252,22 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
       }
       float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       const int e = mx_block_exponent(amax);
       const float inv = mx_inv_scale(e);
-      uint32_t w[8];
+      uint32_t w[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+      for (int k = 0; k < 4; ++k)
         w[k] = e4m3_pack4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
-      uint4* dst = reinterpret_cast<uint4*>(qr + (bz * rows + r) * cols + cc);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      scr[scale_index(GROUPED, bz * rows + r, cc / 32, gridDim.z * rows, cols / 32)] = static_cast<uint8_t>(e + 127);
+      // the row's two scale bytes (blocks c0/32 and c0/32 + 1, adjacent in both scale layouts) from lanes qt = 0, 2
+      const uint32_t pair = static_cast<uint32_t>(e + 127) | (static_cast<uint32_t>(__shfl_xor(e, 2, 64) + 127) << 8);
+      if (r < rows && c0 + qt * 16 < cols) {
+        *reinterpret_cast<uint4*>(qr + (bz * rows + r) * cols + c0 + qt * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (qt == 0)
+          *reinterpret_cast<uint16_t*>(scr + scale_index(GROUPED, bz * rows + r, c0 / 32, gridDim.z * rows, cols / 32)) =
+              static_cast<uint16_t>(pair);
+      }
     }
   }
 }
