@@ -27,6 +27,8 @@ struct FfnArgs {
                            // entry [max_tiles] = {number of live tiles, 0, 0, 0}
   int64_t max_tiles;
   int bm;                  // row-tile height the tile table was built for
+  const int4* tiles128;    // MXFP8 backward with bm = 256: a 128-row table for the SwiGLU-backward GEMM, else null
+  int64_t max_tiles128;
   int E, d, f;
   int64_t R;
   // inputs

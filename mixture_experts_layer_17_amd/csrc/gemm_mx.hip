@@ -540,7 +540,15 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
     if (!dy_mx) launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s, true);
     m.dyq = dy_mx ? dy_mx : b.dy.q;
     m.dys = dy_mx ? dy_mx + align_up(static_cast<size_t>(a.R) * a.d, 256) : b.dy.s;
-    st = launch_mx_kind(kG3, m, max_tiles, s);
+    if (a.tiles128) {  // 128 x 128 tiles for the SwiGLU backward
+      MxArgs m3 = m;
+      m3.f.tiles = a.tiles128;
+      m3.f.max_tiles = a.max_tiles128;
+      m3.f.bm = 128;
+      st = launch_mx_kind(kG3, m3, a.max_tiles128, s);
+    } else {
+      st = launch_mx_kind(kG3, m, max_tiles, s);
+    }
     if (st != MOE_OK) return st;
     // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f
     launch_mx_rows(a.dhg, bf, a.R, a.f, b.dhg.q, b.dhg.s, s, true);
