@@ -17,7 +17,8 @@ namespace {
 constexpr int kChunk = 32;        // tokens per dW_r partial (generic path)
 constexpr int kDwTok = 64;        // tokens per dW_r partial (E <= 16 path)
 constexpr int kDwFeat = 512;      // features per workgroup of the E <= 16 dW_r path (64 lanes x 8)
-constexpr int kTokPerBlk = 16;    // tokens per workgroup in the wave-per-token kernels (4 per wave)
+constexpr int kTokPerBlk = 8;     // tokens per workgroup in the wave-per-token kernels (2 per wave; more
+                                  // per workgroup measured slower: fewer workgroups to hide the loads)
 constexpr int kTokPar = 2;        // tokens a wave works on at once
 constexpr size_t kMaxLdsW = 64 * 1024;
 
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(256) void router_bwd_dw_fast_kernel(const T* __rest
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[q][e] = 0.f;
   if (i0 < d) {
+#pragma unroll 4  // four tokens' loads in flight
     for (int r = wave; r < nt; r += 4) {
       float xv[8];
       const T* xr = x + (t0 + r) * d + i0;
