@@ -187,10 +187,10 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
   const T* base = src + bz * rows * cols;
   for (int v = tid; v < 128 * VPR; v += blockDim.x) {
     const int tr = v / VPR, cv = v - tr * VPR;
-    const int blk = tr >> 5, r = tr & 31;
+    const int bi = tr >> 5, r = tr & 31;
     const int64_t col = c0 + cv * VEC;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < b_nv[blk] && col < cols) val = *reinterpret_cast<const uint4*>(base + (b_r0[blk] + r) * cols + col);
+    if (r < b_nv[bi] && col < cols) val = *reinterpret_cast<const uint4*>(base + (b_r0[bi] + r) * cols + col);
     *reinterpret_cast<uint4*>(tile + tr * LDT + cv * VEC) = val;
   }
   __syncthreads();
