@@ -123,7 +123,12 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
   constexpr int VPR = kColW / VEC;          // vectors per tile row
   constexpr int LDT = kColW + VEC;          // padded tile row (16-byte aligned)
   __shared__ __attribute__((aligned(16))) T tile[128 * LDT];
-  __shared__ uint32_t obuf[kColW][33];      // encoded bytes: 4 blocks x 32 per output row
+  // encoded bytes, 4 blocks x 32 per output row.  Without BOTH they take the
+  // tile's place once every read of it is done (less LDS per workgroup, more
+  // workgroups per CU: measured faster); BOTH still reads the tile afterwards.
+  __shared__ uint32_t obuf_own[BOTH ? kColW : 1][33];
+  static_assert(kColW * 33 * 4 <= 128 * LDT * sizeof(T), "output staging fits the tile");
+  uint32_t (*obuf)[33] = BOTH ? obuf_own : reinterpret_cast<uint32_t (*)[33]>(tile);
   __shared__ uint8_t osc[kColW][4];
   __shared__ int32_t s_off[kMaxE + 1];
   __shared__ int32_t s_blk[kMaxE + 1];
@@ -204,11 +209,13 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     }
     const int e = mx_block_exponent(amax);
     const float inv = mx_inv_scale(e);
+    uint32_t w[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      obuf[lane][wave * 8 + k] =
-          e4m3_pack4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
-    }
+    for (int k = 0; k < 8; ++k)
+      w[k] = e4m3_pack4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
+    if constexpr (!BOTH) __syncthreads();  // the tile is read: obuf takes its place
+#pragma unroll
+    for (int k = 0; k < 8; ++k) obuf[lane][wave * 8 + k] = w[k];
     osc[lane][wave] = static_cast<uint8_t>(e + 127);
   }
   __syncthreads();
