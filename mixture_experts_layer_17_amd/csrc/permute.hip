@@ -51,7 +51,11 @@ __global__ __launch_bounds__(64 * kWaves) void dispatch_kernel(const T* __restri
   }
 }
 
-template <typename T>
+// Up to KP slots per token (k <= KP); every lane loads kBatch 16-byte vectors of
+// each of the k rows before it uses any, so a wave keeps k * kBatch KiB in flight.
+constexpr int kBatch = 4;
+
+template <typename T, int KP>
 __global__ __launch_bounds__(64 * kWaves) void gather_sum_kernel(const T* __restrict__ src_rows, int64_t Tn, int d,
                                                                 int k, const int32_t* __restrict__ perm_dst,
                                                                 const float* __restrict__ gates,
@@ -62,36 +66,45 @@ __global__ __launch_bounds__(64 * kWaves) void gather_sum_kernel(const T* __rest
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nvec = d / V;
-  int rows[kMaxK];
-  float w[kMaxK];
+  const uint4* rows[KP];
+  float w[KP];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    rows[j] = j < k ? perm_dst[t * k + j] : 0;
+  for (int j = 0; j < KP; ++j) {
+    rows[j] = reinterpret_cast<const uint4*>(src_rows + static_cast<int64_t>(j < k ? perm_dst[t * k + j] : 0) * d);
     w[j] = j < k ? (gates ? gates[t * k + j] : 1.0f) : 0.f;
   }
   uint4* dst = reinterpret_cast<uint4*>(out + t * d);
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[V];
+  for (int c0 = 0; c0 < nvec; c0 += 64 * kBatch) {
+    uint4 v[KP][kBatch];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    uint4 v[kMaxK];
+    for (int j = 0; j < KP; ++j)
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) v[j] = reinterpret_cast<const uint4*>(src_rows + static_cast<int64_t>(rows[j]) * d)[c];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        float f[V];
-        Elem<T>::unpack(v[j], f);
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += w[j] * f[i];
+      for (int b = 0; b < kBatch; ++b) {
+        const int c = c0 + b * 64 + lane;
+        if (j < k && c < nvec) v[j][b] = rows[j][c];
       }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * 64 + lane;
+      if (c >= nvec) break;
+      float acc[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        if (j < k) {
+          float f[V];
+          Elem<T>::unpack(v[j][b], f);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] += w[j] * f[i];
+        }
+      }
+      dst[c] = Elem<T>::pack(acc);
     }
-    dst[c] = Elem<T>::pack(acc);
   }
 }
 
-template <typename T>
+template <typename T, int KP>
 __global__ __launch_bounds__(64 * kWaves) void combine_bwd_kernel(const T* __restrict__ dout,
                                                                  const T* __restrict__ y_perm, int64_t Tn, int d,
                                                                  int k, const int32_t* __restrict__ perm_dst,
@@ -102,37 +115,51 @@ __global__ __launch_bounds__(64 * kWaves) void combine_bwd_kernel(const T* __res
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nvec = d / V;
-  int rows[kMaxK];
-  float g[kMaxK], dot[kMaxK];
+  int64_t rows[KP];
+  float g[KP], dot[KP];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    rows[j] = j < k ? perm_dst[t * k + j] : 0;
+  for (int j = 0; j < KP; ++j) {
+    rows[j] = static_cast<int64_t>(j < k ? perm_dst[t * k + j] : 0) * d;
     g[j] = j < k ? gates[t * k + j] : 0.f;
     dot[j] = 0.f;
   }
   const uint4* src = reinterpret_cast<const uint4*>(dout + t * d);
-  for (int c = lane; c < nvec; c += 64) {
-    float o[V];
-    Elem<T>::unpack(src[c], o);
-    uint4 yv[kMaxK];
+  for (int c0 = 0; c0 < nvec; c0 += 64 * kBatch) {
+    uint4 ov[kBatch], yv[KP][kBatch];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) yv[j] = reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[c];
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * 64 + lane;
+      if (c < nvec) ov[b] = src[c];
+    }
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        float y[V], s[V];
-        Elem<T>::unpack(yv[j], y);
-        float p = 0.f;
+    for (int j = 0; j < KP; ++j)
 #pragma unroll
-        for (int i = 0; i < V; ++i) { p += o[i] * y[i]; s[i] = g[j] * o[i]; }
-        dot[j] += p;
-        reinterpret_cast<uint4*>(dy_perm + static_cast<int64_t>(rows[j]) * d)[c] = Elem<T>::pack(s);
+      for (int b = 0; b < kBatch; ++b) {
+        const int c = c0 + b * 64 + lane;
+        if (j < k && c < nvec) yv[j][b] = reinterpret_cast<const uint4*>(y_perm + rows[j])[c];
+      }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * 64 + lane;
+      if (c >= nvec) break;
+      float o[V];
+      Elem<T>::unpack(ov[b], o);
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        if (j < k) {
+          float y[V], sv[V];
+          Elem<T>::unpack(yv[j][b], y);
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < V; ++i) { p += o[i] * y[i]; sv[i] = g[j] * o[i]; }
+          dot[j] += p;
+          reinterpret_cast<uint4*>(dy_perm + rows[j])[c] = Elem<T>::pack(sv);
+        }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KP; ++j) {
     if (j < k) {
       const float s = wave_sum(dot[j]);
       if (lane == 0) dgates[t * k + j] = s;
@@ -215,6 +242,7 @@ __global__ __launch_bounds__(64 * kWaves) void dispatch_mx_kernel(const uint16_t
 // combine_bwd that also writes the MX rows layout of dy_perm (codes and scale
 // words as in dispatch_mx_kernel), encoded from the stored bf16 values.
 // bf16, d % 128 == 0.
+template <int KP>
 __global__ __launch_bounds__(64 * kWaves) void combine_bwd_mx_kernel(
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y_perm, int64_t Tn, int d, int k,
     const int32_t* __restrict__ perm_dst, const float* __restrict__ gates, uint16_t* __restrict__ dy_perm,
@@ -224,50 +252,63 @@ __global__ __launch_bounds__(64 * kWaves) void combine_bwd_mx_kernel(
   if (t >= Tn) return;
   const int64_t R = Tn * k;
   const int nvec = d / 8;
-  int rows[kMaxK];
-  float g[kMaxK], dot[kMaxK];
+  int64_t rows[KP];
+  float g[KP], dot[KP];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KP; ++j) {
     rows[j] = j < k ? perm_dst[t * k + j] : 0;
     g[j] = j < k ? gates[t * k + j] : 0.f;
     dot[j] = 0.f;
   }
   const uint4* src = reinterpret_cast<const uint4*>(dout + t * d);
-  for (int c0 = 0; c0 < nvec; c0 += 64) {  // wave-uniform trip count; groups of 16 lanes are valid together
-    const int c = c0 + lane;
-    const bool ok = c < nvec;
-    float o[8];
-    Elem<uint16_t>::unpack(ok ? src[c] : make_uint4(0, 0, 0, 0), o);
-    uint4 yv[kMaxK];
+  // wave-uniform trip counts; groups of 16 lanes are valid together (d % 128 == 0)
+  for (int c0 = 0; c0 < nvec; c0 += 64 * kBatch) {
+    uint4 ov[kBatch], yv[KP][kBatch];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) yv[j] = ok ? reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(rows[j]) * d)[c]
-                            : make_uint4(0, 0, 0, 0);
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * 64 + lane;
+      ov[b] = c < nvec ? src[c] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        float y[8], sv[8];
-        Elem<uint16_t>::unpack(yv[j], y);
-        float p = 0.f;
+    for (int j = 0; j < KP; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { p += o[i] * y[i]; sv[i] = g[j] * o[i]; }
-        dot[j] += p;
-        const uint4 packed = Elem<uint16_t>::pack(sv);
-        float r[8];
-        Elem<uint16_t>::unpack(packed, r);  // quantise the stored (bf16) values
-        uint32_t word;
-        const uint2 cq = mx_encode8(r, &word, c);
-        if (ok) {
-          const int64_t row = rows[j];
-          reinterpret_cast<uint4*>(dy_perm + row * d)[c] = packed;
-          reinterpret_cast<uint2*>(q + row * d)[c] = cq;
-          if ((c & 15) == 0) sw[static_cast<int64_t>(c >> 4) * R + row] = word;
+      for (int b = 0; b < kBatch; ++b) {
+        const int c = c0 + b * 64 + lane;
+        if (j < k) yv[j][b] = c < nvec ? reinterpret_cast<const uint4*>(y_perm + rows[j] * d)[c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (c0 + b * 64 >= nvec) break;  // wave-uniform
+      const int c = c0 + b * 64 + lane;
+      const bool ok = c < nvec;
+      float o[8];
+      Elem<uint16_t>::unpack(ov[b], o);
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        if (j < k) {
+          float y[8], sv[8];
+          Elem<uint16_t>::unpack(yv[j][b], y);
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { p += o[i] * y[i]; sv[i] = g[j] * o[i]; }
+          dot[j] += p;
+          const uint4 packed = Elem<uint16_t>::pack(sv);
+          float r[8];
+          Elem<uint16_t>::unpack(packed, r);  // quantise the stored (bf16) values
+          uint32_t word;
+          const uint2 cq = mx_encode8(r, &word, c);
+          if (ok) {
+            const int64_t row = rows[j];
+            reinterpret_cast<uint4*>(dy_perm + row * d)[c] = packed;
+            reinterpret_cast<uint2*>(q + row * d)[c] = cq;
+            if ((c & 15) == 0) sw[static_cast<int64_t>(c >> 4) * R + row] = word;
+          }
         }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KP; ++j) {
     if (j < k) {
       const float s = wave_sum(dot[j]);
       if (lane == 0) dgates[t * k + j] = s;
@@ -281,6 +322,32 @@ bool dims_ok(int dtype, int64_t T, int d, int k) {
 }
 
 inline dim3 grid_for(int64_t T) { return dim3(static_cast<unsigned>(cdiv(T, kWaves))); }
+
+// k <= 4 (the workloads' top-4) takes the 4-slot kernels, whose register
+// footprint allows twice the resident waves of the 8-slot ones.
+template <typename T>
+int launch_gather_sum(const char* name, const T* src, int64_t Tn, int d, int k, const int32_t* perm_dst,
+                      const float* gates, T* out, hipStream_t s) {
+  if (k <= 4)
+    MOE_LAUNCH(name, (gather_sum_kernel<T, 4>), grid_for(Tn), dim3(64 * kWaves), 0, s, src, Tn, d, k, perm_dst, gates,
+               out);
+  else
+    MOE_LAUNCH(name, (gather_sum_kernel<T, kMaxK>), grid_for(Tn), dim3(64 * kWaves), 0, s, src, Tn, d, k, perm_dst,
+               gates, out);
+  return launch_status();
+}
+
+template <typename T>
+int launch_combine_bwd(const T* dout, const T* y_perm, int64_t Tn, int d, int k, const int32_t* perm_dst,
+                       const float* gates, T* dy_perm, float* dgates, hipStream_t s) {
+  if (k <= 4)
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, 4>), grid_for(Tn), dim3(64 * kWaves), 0, s, dout, y_perm, Tn, d,
+               k, perm_dst, gates, dy_perm, dgates);
+  else
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, kMaxK>), grid_for(Tn), dim3(64 * kWaves), 0, s, dout, y_perm,
+               Tn, d, k, perm_dst, gates, dy_perm, dgates);
+  return launch_status();
+}
 
 }  // namespace
 }  // namespace moe
@@ -334,10 +401,16 @@ extern "C" int moe_combine_bwd_mx(const void* dout, const void* y_perm, const fl
   const int64_t R = T * k;
   uint8_t* q = static_cast<uint8_t*>(dy_mx);
   uint32_t* sw = reinterpret_cast<uint32_t*>(q + align_up(static_cast<size_t>(R) * d, 256));
-  MOE_LAUNCH("combine_bwd", combine_bwd_mx_kernel, grid_for(T), dim3(64 * kWaves), 0,
-             static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(dout),
-             static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst, gates, static_cast<uint16_t*>(dy_perm), dgates,
-             q, sw);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* dout16 = static_cast<const uint16_t*>(dout);
+  const uint16_t* y16 = static_cast<const uint16_t*>(y_perm);
+  uint16_t* dy16 = static_cast<uint16_t*>(dy_perm);
+  if (k <= 4)
+    MOE_LAUNCH("combine_bwd", combine_bwd_mx_kernel<4>, grid_for(T), dim3(64 * kWaves), 0, s, dout16, y16, T, d, k,
+               perm_dst, gates, dy16, dgates, q, sw);
+  else
+    MOE_LAUNCH("combine_bwd", combine_bwd_mx_kernel<kMaxK>, grid_for(T), dim3(64 * kWaves), 0, s, dout16, y16, T, d,
+               k, perm_dst, gates, dy16, dgates, q, sw);
   return launch_status();
 }
 
@@ -348,13 +421,10 @@ extern "C" int moe_dispatch_bwd(const void* dx_perm, int dtype, int64_t T, int32
   if (!dx_perm || !perm_dst || !dx || !aligned16(dx_perm) || !aligned16(dx)) return MOE_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MOE_F32)
-    MOE_LAUNCH("dispatch_bwd", gather_sum_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const float*>(dx_perm), T, d, k, perm_dst, nullptr, static_cast<float*>(dx));
-  else
-    MOE_LAUNCH("dispatch_bwd", gather_sum_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const uint16_t*>(dx_perm), T, d, k, perm_dst, nullptr,
-                       static_cast<uint16_t*>(dx));
-  return launch_status();
+    return launch_gather_sum("dispatch_bwd", static_cast<const float*>(dx_perm), T, d, k, perm_dst, nullptr,
+                             static_cast<float*>(dx), s);
+  return launch_gather_sum("dispatch_bwd", static_cast<const uint16_t*>(dx_perm), T, d, k, perm_dst, nullptr,
+                           static_cast<uint16_t*>(dx), s);
 }
 
 extern "C" int moe_combine(const void* y_perm, int dtype, const float* gates, const int32_t* perm_dst, int64_t T,
@@ -364,12 +434,10 @@ extern "C" int moe_combine(const void* y_perm, int dtype, const float* gates, co
   if (!y_perm || !gates || !perm_dst || !out || !aligned16(y_perm) || !aligned16(out)) return MOE_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MOE_F32)
-    MOE_LAUNCH("combine", gather_sum_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const float*>(y_perm), T, d, k, perm_dst, gates, static_cast<float*>(out));
-  else
-    MOE_LAUNCH("combine", gather_sum_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst, gates, static_cast<uint16_t*>(out));
-  return launch_status();
+    return launch_gather_sum("combine", static_cast<const float*>(y_perm), T, d, k, perm_dst, gates,
+                             static_cast<float*>(out), s);
+  return launch_gather_sum("combine", static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst, gates,
+                           static_cast<uint16_t*>(out), s);
 }
 
 extern "C" int moe_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* gates,
@@ -382,12 +450,8 @@ extern "C" int moe_combine_bwd(const void* dout, const void* y_perm, int dtype, 
     return MOE_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MOE_F32)
-    MOE_LAUNCH("combine_bwd", combine_bwd_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const float*>(dout), static_cast<const float*>(y_perm), T, d, k, perm_dst, gates,
-                       static_cast<float*>(dy_perm), dgates);
-  else
-    MOE_LAUNCH("combine_bwd", combine_bwd_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst,
-                       gates, static_cast<uint16_t*>(dy_perm), dgates);
-  return launch_status();
+    return launch_combine_bwd(static_cast<const float*>(dout), static_cast<const float*>(y_perm), T, d, k, perm_dst,
+                              gates, static_cast<float*>(dy_perm), dgates, s);
+  return launch_combine_bwd(static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y_perm), T, d, k,
+                            perm_dst, gates, static_cast<uint16_t*>(dy_perm), dgates, s);
 }
