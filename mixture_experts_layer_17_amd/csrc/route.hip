@@ -23,7 +23,9 @@ namespace {
 
 constexpr int kTokPerBlk = 64;   // tokens per routing block (one wave)
 constexpr int kStageMaxE = 128;  // widest logit row staged through LDS
+constexpr int kStageBatch = 8;   // 16-byte logit loads per lane in flight while staging
 constexpr int kScanThreads = 1024;
+constexpr int kScanBatch = 8;    // block counts per thread loaded before any is used
 
 template <int K>
 __global__ __launch_bounds__(64) void route_select_kernel(const float* __restrict__ logits, int64_t T,
@@ -46,8 +48,34 @@ __global__ __launch_bounds__(64) void route_select_kernel(const float* __restric
 
   const float* src = logits + t0 * E;
   if (stage) {
+    // 16-byte loads, kStageBatch per lane issued before any is written to LDS
+    // (src is 16-byte aligned when logits is: t0 * E * 4 is a multiple of 256)
     const int nel = ntok * E;
-    for (int i = lane; i < nel; i += 64) {
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    const int nv = vec ? nel / 4 : 0;
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    for (int v0 = 0; v0 < nv; v0 += 64 * kStageBatch) {
+      float4 buf[kStageBatch];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < nv) buf[u] = s4[v];
+      }
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < nv) {
+          int r = (4 * v) / E, c = 4 * v - r * E;
+          const float f[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            tile[r * ld + c] = f[q];
+            if (++c == E) { c = 0; ++r; }
+          }
+        }
+      }
+    }
+    for (int i = 4 * nv + lane; i < nel; i += 64) {
       const int r = i / E;
       tile[r * ld + (i - r * E)] = src[i];
     }
@@ -116,6 +144,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
   __shared__ int32_t part[kScanThreads];
   __shared__ int32_t tot[kMaxE + 1];
   __shared__ int32_t mxb[kMaxE + 1];
+  __shared__ int32_t sc[2][kMaxE], scb[2][kMaxE];
   const int tid = threadIdx.x;
   const int parts = kScanThreads / E;  // >= 4 for E <= 256
   const int e = tid % E;
@@ -126,25 +155,41 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
   const int b1 = active ? min(nblk, b0 + per) : 0;
   int s = 0;
   if (active)
-    for (int b = b0; b < b1; ++b) s += blk[static_cast<int64_t>(b) * E + e];
+    for (int b = b0; b < b1; b += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) c[u] = b + u < b1 ? blk[static_cast<int64_t>(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) s += c[u];
+    }
   part[tid] = s;
   __syncthreads();
+  // per-expert totals, then exclusive scans over the E (<= 256) experts:
+  // Hillis-Steele in LDS (integer sums, so the order of additions is immaterial)
+  int own = 0, ownb = 0;
   if (tid < E) {
-    int acc = 0;
-    for (int q = 0; q < parts; ++q) acc += part[q * E + tid];
-    tot[tid] = acc;
-    mxb[tid] = (acc + 31) / 32;
+    for (int q = 0; q < parts; ++q) own += part[q * E + tid];
+    ownb = (own + 31) / 32;
+    sc[0][tid] = own;
+    scb[0][tid] = ownb;
   }
   __syncthreads();
-  if (tid == 0) {
-    // E <= 256: a serial exclusive scan is short and exactly ordered.
-    int run = 0, runb = 0;
-    for (int x = 0; x < E; ++x) {
-      const int c = tot[x], cb = mxb[x];
-      tot[x] = run; mxb[x] = runb;
-      run += c; runb += cb;
+  int cur = 0;
+  for (int o = 1; o < E; o <<= 1) {
+    if (tid < E) {
+      sc[cur ^ 1][tid] = sc[cur][tid] + (tid >= o ? sc[cur][tid - o] : 0);
+      scb[cur ^ 1][tid] = scb[cur][tid] + (tid >= o ? scb[cur][tid - o] : 0);
     }
-    tot[E] = run; mxb[E] = runb;
+    __syncthreads();
+    cur ^= 1;
+  }
+  if (tid < E) {
+    tot[tid] = sc[cur][tid] - own;
+    mxb[tid] = scb[cur][tid] - ownb;
+    if (tid == E - 1) {
+      tot[E] = sc[cur][tid];
+      mxb[E] = scb[cur][tid];
+    }
   }
   __syncthreads();
   if (tid <= E) {
@@ -156,11 +201,16 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
   if (active) {
     int base = tot[e];
     for (int q = 0; q < p; ++q) base += part[q * E + e];
-    for (int b = b0; b < b1; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * E + e;
-      const int c = blk[i];
-      blk[i] = base;
-      base += c;
+    for (int b = b0; b < b1; b += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) c[u] = b + u < b1 ? blk[static_cast<int64_t>(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        if (b + u < b1) {
+          blk[static_cast<int64_t>(b + u) * E + e] = base;
+          base += c[u];
+        }
     }
   }
 }

@@ -20,6 +20,8 @@ constexpr int kDwFeat = 512;      // features per workgroup of the E <= 16 dW_r 
 constexpr int kTokPerBlk = 8;     // tokens per workgroup in the wave-per-token kernels (2 per wave; more
                                   // per workgroup measured slower: fewer workgroups to hide the loads)
 constexpr int kTokPar = 2;        // tokens a wave works on at once
+constexpr int kXBatch = 4;        // 16-byte activation vectors per lane and token loaded before any is used
+constexpr int kDwBatch = 4;       // tokens per wave whose activation loads are in flight together (dW_r)
 constexpr size_t kMaxLdsW = 64 * 1024;
 
 // W_r [d, E] in LDS, widened per read.  Feature i = V*c + q (c: 16-byte vector
@@ -82,26 +84,32 @@ __global__ __launch_bounds__(256) void router_fwd_fast_kernel(const T* __restric
     for (int p = 0; p < kTokPar; ++p)
 #pragma unroll
       for (int e = 0; e < EP; ++e) acc[p][e] = 0.f;
-    for (int c = lane; c < nvec; c += 64) {
-      float xv[kTokPar][V];
+    for (int c0 = lane; c0 < nvec; c0 += 64 * kXBatch) {
+      uint4 raw[kXBatch][kTokPar];  // every load of the batch in flight before the first is used
 #pragma unroll
-      for (int p = 0; p < kTokPar; ++p) {
-        const int64_t t = tw + tt + p;
-        if (t < Tn) {
-          Elem<T>::unpack(reinterpret_cast<const uint4*>(x + t * d)[c], xv[p]);
-        } else {
+      for (int b = 0; b < kXBatch; ++b)
 #pragma unroll
-          for (int q = 0; q < V; ++q) xv[p][q] = 0.f;
+        for (int p = 0; p < kTokPar; ++p) {
+          const int64_t t = tw + tt + p;
+          const int c = c0 + b * 64;
+          raw[b][p] = (t < Tn && c < nvec) ? reinterpret_cast<const uint4*>(x + t * d)[c] : make_uint4(0, 0, 0, 0);
         }
-      }
 #pragma unroll
-      for (int q = 0; q < V; ++q) {
-        float wr[EP];
-        w_row<T, EP>(wl, nvec, c, q, wr);
+      for (int b = 0; b < kXBatch; ++b) {
+        const int c = c0 + b * 64;
+        if (c >= nvec) break;
+        float xv[kTokPar][V];
 #pragma unroll
-        for (int p = 0; p < kTokPar; ++p)
+        for (int p = 0; p < kTokPar; ++p) Elem<T>::unpack(raw[b][p], xv[p]);
 #pragma unroll
-          for (int e = 0; e < EP; ++e) acc[p][e] += xv[p][q] * wr[e];
+        for (int q = 0; q < V; ++q) {
+          float wr[EP];
+          w_row<T, EP>(wl, nvec, c, q, wr);
+#pragma unroll
+          for (int p = 0; p < kTokPar; ++p)
+#pragma unroll
+            for (int e = 0; e < EP; ++e) acc[p][e] += xv[p][q] * wr[e];
+        }
       }
     }
 #pragma unroll
@@ -139,34 +147,41 @@ __global__ __launch_bounds__(256) void router_bwd_dx_fast_kernel(const float* __
 #pragma unroll
       for (int e = 0; e < EP; ++e) g[p][e] = (t < Tn && e < E) ? dl[t * E + e] : 0.f;
     }
-    for (int c = lane; c < nvec; c += 64) {
-      float o[kTokPar][V];
+    for (int c0 = lane; c0 < nvec; c0 += 64 * kXBatch) {
+      uint4 raw[kXBatch][kTokPar];  // the batch's dx loads in flight before the first is used
 #pragma unroll
-      for (int p = 0; p < kTokPar; ++p) {
-        const int64_t t = tw + tt + p;
-        if (accumulate && t < Tn) {
-          Elem<T>::unpack(reinterpret_cast<const uint4*>(dx + t * d)[c], o[p]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < V; ++q) o[p][q] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < V; ++q) {
-        float wr[EP];
-        w_row<T, EP>(wl, nvec, c, q, wr);
+      for (int b = 0; b < kXBatch; ++b)
 #pragma unroll
         for (int p = 0; p < kTokPar; ++p) {
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < EP; ++e) s += g[p][e] * wr[e];
-          o[p][q] += s;
+          const int64_t t = tw + tt + p;
+          const int c = c0 + b * 64;
+          raw[b][p] = (accumulate && t < Tn && c < nvec) ? reinterpret_cast<const uint4*>(dx + t * d)[c]
+                                                        : make_uint4(0, 0, 0, 0);
         }
-      }
 #pragma unroll
-      for (int p = 0; p < kTokPar; ++p) {
-        const int64_t t = tw + tt + p;
-        if (t < Tn) reinterpret_cast<uint4*>(dx + t * d)[c] = Elem<T>::pack(o[p]);
+      for (int b = 0; b < kXBatch; ++b) {
+        const int c = c0 + b * 64;
+        if (c >= nvec) break;
+        float o[kTokPar][V];
+#pragma unroll
+        for (int p = 0; p < kTokPar; ++p) Elem<T>::unpack(raw[b][p], o[p]);
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          float wr[EP];
+          w_row<T, EP>(wl, nvec, c, q, wr);
+#pragma unroll
+          for (int p = 0; p < kTokPar; ++p) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < EP; ++e) s += g[p][e] * wr[e];
+            o[p][q] += s;
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < kTokPar; ++p) {
+          const int64_t t = tw + tt + p;
+          if (t < Tn) reinterpret_cast<uint4*>(dx + t * d)[c] = Elem<T>::pack(o[p]);
+        }
       }
     }
   }
@@ -200,20 +215,29 @@ __global__ __launch_bounds__(256) void router_bwd_dw_fast_kernel(const T* __rest
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[q][e] = 0.f;
   if (i0 < d) {
-#pragma unroll 4  // four tokens' loads in flight
-    for (int r = wave; r < nt; r += 4) {
-      float xv[8];
-      const T* xr = x + (t0 + r) * d + i0;
-      if constexpr (sizeof(T) == 2) {
-        Elem<T>::unpack(*reinterpret_cast<const uint4*>(xr), xv);
-      } else {
-        Elem<T>::unpack(reinterpret_cast<const uint4*>(xr)[0], xv);
-        Elem<T>::unpack(reinterpret_cast<const uint4*>(xr)[1], xv + 4);
+    // tokens wave, wave + 4, ...: kDwBatch tokens' loads in flight before the first is used
+    constexpr int NV = sizeof(T) == 2 ? 1 : 2;  // 16-byte vectors per 8 features
+    for (int r0 = wave; r0 < nt; r0 += 4 * kDwBatch) {
+      uint4 raw[kDwBatch][NV];
+#pragma unroll
+      for (int b = 0; b < kDwBatch; ++b) {
+        const int r = r0 + 4 * b;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          raw[b][v] = r < nt ? reinterpret_cast<const uint4*>(x + (t0 + r) * d + i0)[v] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int b = 0; b < kDwBatch; ++b) {
+        const int r = r0 + 4 * b;
+        if (r >= nt) break;
+        float xv[8];
 #pragma unroll
-        for (int e = 0; e < EP; ++e) acc[q][e] += xv[q] * dls[r * EP + e];
+        for (int v = 0; v < NV; ++v) Elem<T>::unpack(raw[b][v], xv + v * (8 / NV));
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int e = 0; e < EP; ++e) acc[q][e] += xv[q] * dls[r * EP + e];
+      }
     }
   }
   float* out = part + (c * ng + fg) * static_cast<int64_t>(kDwFeat * EP);

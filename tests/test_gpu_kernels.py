@@ -29,7 +29,8 @@ def _adversarial(T, E, seed):
 
 
 ROUTE_CASES = [(1, 8, 2), (63, 8, 4), (64, 8, 4), (65, 16, 4), (1000, 128, 4), (4097, 256, 8), (200, 1, 1),
-               (130, 8, 8), (16384, 128, 4)]
+               (130, 8, 8), (16384, 128, 4),
+               (203, 1, 1), (7, 3, 2), (129, 5, 3)]  # logit tiles whose size is not a multiple of four
 
 
 @pytest.mark.parametrize("T,E,k", ROUTE_CASES)
@@ -60,6 +61,24 @@ def test_route_stats_bit_exact(gpu, T, E, k, bias):
     torch.cuda.synchronize()
     ref = mo.routing_stats(mo.routing_metadata(mo.topk_select(lg, k), E)["counts"])
     np.testing.assert_array_equal(st.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,E,k", [(1000, 128, 4), (203, 5, 3)])
+def test_route_topk_unaligned_logits(gpu, T, E, k):
+    """Logits at a 4-byte (not 16-byte) aligned address take the scalar staging loads: same routing."""
+    gu.say(f"case route unaligned T={T} E={E} k={k}")
+    lg = np.random.default_rng(T + 5 * E).standard_normal((T, E)).astype(np.float32)
+    flat = torch.empty(T * E + 1, dtype=torch.float32, device="cuda")
+    view = flat[1:].view(T, E)
+    view.copy_(torch.from_numpy(lg))
+    assert view.data_ptr() % 16 != 0
+    out = B.moe_route_topk(view, k)
+    torch.cuda.synchronize()
+    idx = mo.topk_select(lg, k)
+    meta = mo.routing_metadata(idx, E)
+    np.testing.assert_array_equal(out["topk_idx"].cpu().numpy(), idx)
+    for key in ("counts", "offsets", "perm_src", "perm_dst", "mx_blk_offsets"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), meta[key], err_msg=key)
 
 
 def test_route_topk_empty_batch(gpu):
