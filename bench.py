@@ -203,8 +203,8 @@ def main() -> int:
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU are not "
-              "part of this build (no collectives, no sharding). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU's share of the MoE layer; the library has no multi-GPU path "
+              "(no collectives, no expert sharding), so only --gpus 1 runs.", file=sys.stderr)
         return 2
 
     import torch
