@@ -89,6 +89,30 @@ def test_route_topk_empty_batch(gpu):
     assert out["counts"].cpu().numpy().tolist() == [0] * 16
 
 
+@pytest.mark.parametrize("prec", ["f32", "bf16", "mxfp8"])
+def test_grouped_ffn_empty_batch(gpu, prec):
+    """No routed rows (R = 0): the forward has nothing to write and the backward overwrites every expert's
+    weight gradients with exact zeros (the buffers start out holding a non-zero pattern)."""
+    gu.say(f"case ffn empty batch {prec}")
+    E, d, f = 4, 256, 256
+    dt = torch.float32 if prec == "f32" else torch.bfloat16
+    gen = torch.Generator().manual_seed(5)
+    w = [(0.02 * torch.randn((E, d, f), generator=gen)).to(dt).cuda(),
+         (0.02 * torch.randn((E, d, f), generator=gen)).to(dt).cuda(),
+         (0.02 * torch.randn((E, f, d), generator=gen)).to(dt).cuda()]
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    x = torch.empty((0, d), dtype=dt, device="cuda")
+    fwd = B.moe_grouped_ffn_fwd(x, offsets, *w, prec)
+    grads = {"dx_perm": torch.empty((0, d), dtype=dt, device="cuda"),
+             "dw_gate": torch.full_like(w[0], 7.0), "dw_up": torch.full_like(w[1], 7.0),
+             "dw_down": torch.full_like(w[2], 7.0)}
+    B.moe_grouped_ffn_bwd(torch.empty((0, d), dtype=dt, device="cuda"), x, fwd["h_gate"], fwd["h_up"], fwd["a_act"],
+                          offsets, offsets, *w, prec, out=grads)
+    torch.cuda.synchronize()
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        assert torch.count_nonzero(grads[key]).item() == 0, key
+
+
 @pytest.mark.parametrize("T,E,k", [(300, 8, 2), (1000, 128, 4), (77, 256, 8)])
 def test_route_topk_bwd(gpu, T, E, k):
     r = np.random.default_rng(3)
