@@ -126,6 +126,121 @@ __global__ __launch_bounds__(256) void router_fwd_fast_kernel(const T* __restric
   }
 }
 
+// bf16 logits on the packed dot product v_dot2_f32_bf16 (two bf16 products and
+// an fp32 accumulate per instruction; the products of bf16 values are exact in
+// fp32).  W_r is staged as pairs of consecutive features: the 32-bit word for
+// expert e and feature pair (8c + 2pp, 8c + 2pp + 1) holds both bf16 values, so
+// an activation word (two consecutive features) meets its weights without any
+// unpacking.  Words for experts 4h .. 4h+3 form one 16-byte vector at
+// ((h * 4 + pp) * nvec + c): the lanes of a wave (consecutive c) read
+// consecutive vectors.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int EP>
+__device__ __forceinline__ void stage_w_pairs(const uint16_t* __restrict__ w, int d, int E, uint4* wl) {
+  static_assert(EP % 4 == 0, "whole 16-byte vectors of expert words");
+  const int nvec = d / 8;
+  const int npair = d / 2;
+  if (E == EP) {
+    // rows i, i + 1 of W_r are EP bf16 each (whole 16-byte vectors)
+    constexpr int P = EP / 8;  // 16-byte vectors per row
+    for (int m = threadIdx.x; m < npair; m += blockDim.x) {
+      const int c = m >> 2, pp = m & 3;
+      const uint4* r0 = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(2 * m) * EP);
+      const uint4* r1 = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(2 * m + 1) * EP);
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const uint4 a = r0[u], b = r1[u];
+        // experts 8u .. 8u+3 from words x, y; 8u+4 .. 8u+7 from z, w
+        const uint4 lo = make_uint4((a.x & 0xFFFFu) | (b.x << 16), (a.x >> 16) | (b.x & 0xFFFF0000u),
+                                    (a.y & 0xFFFFu) | (b.y << 16), (a.y >> 16) | (b.y & 0xFFFF0000u));
+        const uint4 hi = make_uint4((a.z & 0xFFFFu) | (b.z << 16), (a.z >> 16) | (b.z & 0xFFFF0000u),
+                                    (a.w & 0xFFFFu) | (b.w << 16), (a.w >> 16) | (b.w & 0xFFFF0000u));
+        wl[((2 * u) * 4 + pp) * nvec + c] = lo;
+        wl[((2 * u + 1) * 4 + pp) * nvec + c] = hi;
+      }
+    }
+  } else {
+    uint32_t* ww = reinterpret_cast<uint32_t*>(wl);
+    for (int i = threadIdx.x; i < npair * EP; i += blockDim.x) {
+      const int m = i / EP, e = i - m * EP;
+      const int c = m >> 2, pp = m & 3, h = e >> 2, j = e & 3;
+      uint32_t word = 0;
+      if (e < E)
+        word = static_cast<uint32_t>(w[static_cast<int64_t>(2 * m) * E + e]) |
+               (static_cast<uint32_t>(w[static_cast<int64_t>(2 * m + 1) * E + e]) << 16);
+      ww[((h * 4 + pp) * nvec + c) * 4 + j] = word;
+    }
+  }
+  __syncthreads();
+}
+
+template <int EP>
+__global__ __launch_bounds__(256) void router_fwd_dot2_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ w, int64_t Tn, int d,
+                                                             int E, float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  uint4* wl = reinterpret_cast<uint4*>(smem_raw);
+  stage_w_pairs<EP>(w, d, E, wl);
+  constexpr int kPerWave = kTokPerBlk / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nvec = d / 8;
+  const int64_t tw = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + wave * kPerWave;
+  for (int tt = 0; tt < kPerWave; tt += kTokPar) {
+    float acc[kTokPar][EP];
+#pragma unroll
+    for (int p = 0; p < kTokPar; ++p)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) acc[p][e] = 0.f;
+    for (int c0 = lane; c0 < nvec; c0 += 64 * kXBatch) {
+      uint4 raw[kXBatch][kTokPar];  // every load of the batch in flight before the first is used
+#pragma unroll
+      for (int b = 0; b < kXBatch; ++b)
+#pragma unroll
+        for (int p = 0; p < kTokPar; ++p) {
+          const int64_t t = tw + tt + p;
+          const int c = c0 + b * 64;
+          raw[b][p] = (t < Tn && c < nvec) ? reinterpret_cast<const uint4*>(x + t * d)[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+      for (int b = 0; b < kXBatch; ++b) {
+        const int c = c0 + b * 64;
+        if (c >= nvec) break;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+          for (int h = 0; h < EP / 4; ++h) {
+            const uint4 wq = wl[(h * 4 + pp) * nvec + c];
+#pragma unroll
+            for (int p = 0; p < kTokPar; ++p) {
+              const uint32_t xw = pp == 0 ? raw[b][p].x : pp == 1 ? raw[b][p].y : pp == 2 ? raw[b][p].z : raw[b][p].w;
+              acc[p][4 * h + 0] = dot2_bf16(xw, wq.x, acc[p][4 * h + 0]);
+              acc[p][4 * h + 1] = dot2_bf16(xw, wq.y, acc[p][4 * h + 1]);
+              acc[p][4 * h + 2] = dot2_bf16(xw, wq.z, acc[p][4 * h + 2]);
+              acc[p][4 * h + 3] = dot2_bf16(xw, wq.w, acc[p][4 * h + 3]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kTokPar; ++p) {
+      const int64_t t = tw + tt + p;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) acc[p][e] = wave_sum(acc[p][e]);
+      if (t < Tn) {
+#pragma unroll
+        for (int e = 0; e < EP; ++e)
+          if (lane == e && e < E) logits[t * E + e] = acc[p][e];
+      }
+    }
+  }
+}
+
 // dx (+)= dl W_r^T: a wave takes kTokPar tokens at a time, 16-byte output vectors.
 template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_bwd_dx_fast_kernel(const float* __restrict__ dl,
@@ -369,6 +484,17 @@ bool fast_ok(int d, int E) {
 template <typename T>
 int router_fwd_impl(const void* x, const void* w_r, int64_t Tn, int d, int E, float* logits, hipStream_t s) {
   const dim3 g(static_cast<unsigned>(cdiv(Tn, kTokPerBlk)));
+  if constexpr (sizeof(T) == 2) {  // bf16: packed dot products on bf16 pairs
+    if (fast_ok<T, 8>(d, E) || fast_ok<T, 16>(d, E)) {
+      if (E <= 8)
+        MOE_LAUNCH("router_logits", router_fwd_dot2_kernel<8>, g, dim3(256), static_cast<size_t>(d) * 8 * 2, s,
+                   static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), Tn, d, E, logits);
+      else
+        MOE_LAUNCH("router_logits", router_fwd_dot2_kernel<16>, g, dim3(256), static_cast<size_t>(d) * 16 * 2, s,
+                   static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), Tn, d, E, logits);
+      return launch_status();
+    }
+  }
   if (fast_ok<T, 8>(d, E)) {
     MOE_LAUNCH("router_logits", (router_fwd_fast_kernel<T, 8>), g, dim3(256), static_cast<size_t>(d) * 8 * sizeof(T),
                s, static_cast<const T*>(x), static_cast<const T*>(w_r), Tn, d, E, logits);

@@ -223,7 +223,9 @@ def test_router_logits_and_backward(gpu, dtype, case):
     dw = B.moe_router_logits_bwd(xd, wd_, dld, dx, accumulate_dx=acc)
     torch.cuda.synchronize()
     xf, wf = x.float().numpy(), w.float().numpy()
-    assert gu.rel_err(gu.host(lg), mo.router_logits(xf, wf)) <= 1e-5
+    err = gu.rel_err(gu.host(lg), mo.router_logits(xf, wf))
+    print(f"  logits rel err {err:.2e}", flush=True)
+    assert err <= 1e-5
     rdx, rdw = mo.router_logits_backward(xf, wf, dl.numpy())
     tol = 1e-5 if dtype == torch.float32 else 1e-2
     want_dx = (dx0.float().numpy() + rdx) if acc else rdx
