@@ -43,12 +43,24 @@ __device__ __forceinline__ void stage_w(const T* __restrict__ w, int d, int E, T
   if (E == EP) {
     // rows of W_r are whole 16-byte vectors: one vector load per (row, part)
     constexpr int P = EP / V;  // vectors per row
+    constexpr int NB = 8;      // vectors per thread whose loads are in flight together
     const uint4* src = reinterpret_cast<const uint4*>(w);
-#pragma unroll 8
-    for (int i = threadIdx.x; i < d * P; i += blockDim.x) {
-      const int r = i / P, u = i - r * P;
-      const int c = r / V, q = r - c * V;
-      reinterpret_cast<uint4*>(wl + (static_cast<int64_t>(q) * nvec + c) * EP)[u] = src[i];
+    const int n = d * P;
+    for (int i0 = threadIdx.x; i0 < n; i0 += NB * blockDim.x) {
+      uint4 v[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = i0 + b * blockDim.x;
+        v[b] = i < n ? src[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = i0 + b * blockDim.x;
+        if (i >= n) break;
+        const int r = i / P, u = i - r * P;
+        const int c = r / V, q = r - c * V;
+        reinterpret_cast<uint4*>(wl + (static_cast<int64_t>(q) * nvec + c) * EP)[u] = v[b];
+      }
     }
     __syncthreads();
     return;
@@ -248,12 +260,25 @@ __global__ __launch_bounds__(256) void router_bwd_dx_fast_kernel(const float* __
                                                                 T* __restrict__ dx, int accumulate) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   T* wl = reinterpret_cast<T*>(smem_raw);
-  stage_w<T, EP>(w, d, E, wl);
   constexpr int V = Elem<T>::kVec;
   constexpr int kPerWave = kTokPerBlk / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvec = d / V;
   const int64_t tw = static_cast<int64_t>(blockIdx.x) * kTokPerBlk + wave * kPerWave;
+  uint4 raw[kXBatch][kTokPar];  // a batch's dx loads in flight before the first is used
+  auto load_batch = [&](int tt, int c0) {
+#pragma unroll
+    for (int b = 0; b < kXBatch; ++b)
+#pragma unroll
+      for (int p = 0; p < kTokPar; ++p) {
+        const int64_t t = tw + tt + p;
+        const int c = c0 + b * 64;
+        raw[b][p] = (accumulate && t < Tn && c < nvec) ? reinterpret_cast<const uint4*>(dx + t * d)[c]
+                                                      : make_uint4(0, 0, 0, 0);
+      }
+  };
+  load_batch(0, lane);  // the first batch is in flight while W_r is staged
+  stage_w<T, EP>(w, d, E, wl);
   for (int tt = 0; tt < kPerWave; tt += kTokPar) {
     float g[kTokPar][EP];
 #pragma unroll
@@ -263,16 +288,7 @@ __global__ __launch_bounds__(256) void router_bwd_dx_fast_kernel(const float* __
       for (int e = 0; e < EP; ++e) g[p][e] = (t < Tn && e < E) ? dl[t * E + e] : 0.f;
     }
     for (int c0 = lane; c0 < nvec; c0 += 64 * kXBatch) {
-      uint4 raw[kXBatch][kTokPar];  // the batch's dx loads in flight before the first is used
-#pragma unroll
-      for (int b = 0; b < kXBatch; ++b)
-#pragma unroll
-        for (int p = 0; p < kTokPar; ++p) {
-          const int64_t t = tw + tt + p;
-          const int c = c0 + b * 64;
-          raw[b][p] = (accumulate && t < Tn && c < nvec) ? reinterpret_cast<const uint4*>(dx + t * d)[c]
-                                                        : make_uint4(0, 0, 0, 0);
-        }
+      if (tt != 0 || c0 != lane) load_batch(tt, c0);
 #pragma unroll
       for (int b = 0; b < kXBatch; ++b) {
         const int c = c0 + b * 64;
@@ -369,30 +385,44 @@ __global__ __launch_bounds__(256) void router_bwd_dw_fast_kernel(const T* __rest
   }
 }
 
-// Sum of the E <= 16 partials in chunk order; thread j follows the partial layout.
+// Sum of the E <= 16 partials over the chunks.  A workgroup takes 64 outputs j
+// (the partial layout's order); wave s sums the chunks c = s (mod 4) in
+// increasing order, kReduceBatch loads in flight per lane, and the four wave
+// sums are added in wave order: a fixed order, so identical inputs give
+// identical bits.
+constexpr int kReduceBatch = 16;
+
 template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_bwd_dw_fast_reduce_kernel(const float* __restrict__ part, int nchunk,
                                                                        int ng, int d, int E, T* __restrict__ dw) {
+  __shared__ float red[4][64];
   const int64_t per = static_cast<int64_t>(ng) * kDwFeat * EP;
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= per) return;
+  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  float acc = 0.f;
+  if (j < per) {
+    for (int c0 = s; c0 < nchunk; c0 += 4 * kReduceBatch) {
+      float v[kReduceBatch];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u) {
+        const int c = c0 + 4 * u;
+        v[u] = c < nchunk ? part[c * per + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (c0 + 4 * u < nchunk) acc += v[u];
+    }
+  }
+  red[s][lane] = acc;
+  __syncthreads();
+  if (s != 0 || j >= per) return;
   const int e = static_cast<int>(j % EP);
   const int l = static_cast<int>((j / EP) % 64);
   const int q = static_cast<int>((j / (EP * 64)) % 8);
   const int fg = static_cast<int>(j / (EP * kDwFeat));
   const int i = fg * kDwFeat + l * 8 + q;
   if (e >= E || i >= d) return;
-  float acc = 0.f;
-  int c = 0;
-  for (; c + 8 <= nchunk; c += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part[(c + u) * per + j];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
-  }
-  for (; c < nchunk; ++c) acc += part[c * per + j];
-  Elem<T>::store1(dw, static_cast<int64_t>(i) * E + e, acc);
+  Elem<T>::store1(dw, static_cast<int64_t>(i) * E + e, ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
 }
 
 template <typename T>
@@ -524,7 +554,7 @@ void router_bwd_fast(const void* x, const void* w_r, const float* dlogits, int64
              static_cast<const T*>(x), dlogits, Tn, d, E, part);
   const int64_t per = static_cast<int64_t>(ng) * kDwFeat * EP;
   MOE_LAUNCH("router_bwd_dw_reduce", (router_bwd_dw_fast_reduce_kernel<T, EP>),
-             dim3(static_cast<unsigned>(cdiv(per, 256))), dim3(256), 0, s, part, nchunk, ng, d, E,
+             dim3(static_cast<unsigned>(cdiv(per, 64))), dim3(256), 0, s, part, nchunk, ng, d, E,
              static_cast<T*>(dw_r));
 }
 
