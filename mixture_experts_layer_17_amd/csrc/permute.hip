@@ -17,14 +17,15 @@ namespace moe {
 namespace {
 
 constexpr int kWaves = 4;       // tokens per workgroup
+constexpr int kDispatchWaves = 8;  // tokens per workgroup of the plain dispatch (measured 4-5% faster than 4)
 constexpr int kMaxChunks = 16;  // 16-byte vectors per lane held in registers (d <= 8192 bf16)
 
 template <typename T>
-__global__ __launch_bounds__(64 * kWaves) void dispatch_kernel(const T* __restrict__ x, int64_t Tn, int d, int k,
-                                                              const int32_t* __restrict__ perm_dst,
-                                                              T* __restrict__ x_perm) {
+__global__ __launch_bounds__(64 * kDispatchWaves) void dispatch_kernel(const T* __restrict__ x, int64_t Tn, int d,
+                                                                      int k, const int32_t* __restrict__ perm_dst,
+                                                                      T* __restrict__ x_perm) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kDispatchWaves + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nvec = d / Elem<T>::kVec;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
@@ -360,12 +361,13 @@ extern "C" int moe_dispatch(const void* x, int dtype, int64_t T, int32_t d, int3
   if (T == 0) return MOE_OK;
   if (!x || !perm_dst || !x_perm || !aligned16(x) || !aligned16(x_perm)) return MOE_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(cdiv(T, kDispatchWaves)));
   if (dtype == MOE_F32)
-    MOE_LAUNCH("dispatch", dispatch_kernel<float>, grid_for(T), dim3(64 * kWaves), 0, s, static_cast<const float*>(x), T,
-                       d, k, perm_dst, static_cast<float*>(x_perm));
+    MOE_LAUNCH("dispatch", dispatch_kernel<float>, grid, dim3(64 * kDispatchWaves), 0, s, static_cast<const float*>(x),
+               T, d, k, perm_dst, static_cast<float*>(x_perm));
   else
-    MOE_LAUNCH("dispatch", dispatch_kernel<uint16_t>, grid_for(T), dim3(64 * kWaves), 0, s,
-                       static_cast<const uint16_t*>(x), T, d, k, perm_dst, static_cast<uint16_t*>(x_perm));
+    MOE_LAUNCH("dispatch", dispatch_kernel<uint16_t>, grid, dim3(64 * kDispatchWaves), 0, s,
+               static_cast<const uint16_t*>(x), T, d, k, perm_dst, static_cast<uint16_t*>(x_perm));
   return launch_status();
 }
 
