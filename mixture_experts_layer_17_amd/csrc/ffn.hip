@@ -264,11 +264,11 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   }
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
   int st = MOE_OK;
-  if (R > 0) {
-    st = launch(kG3, a, mt, s);
-    if (st == MOE_OK) st = launch(kG5, a, mt, s);
-  }
+  // G5 last: its dX rows (ordinary stores) are then still in the caches when
+  // the dispatch backward reads them right after (3-4% faster than G5 before G6)
+  if (R > 0) st = launch(kG3, a, mt, s);
   if (st == MOE_OK) st = launch(kG4, a, mt, s);
   if (st == MOE_OK) st = launch(kG6, a, mt, s);
+  if (R > 0 && st == MOE_OK) st = launch(kG5, a, mt, s);
   return st;
 }

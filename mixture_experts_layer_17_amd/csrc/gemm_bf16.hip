@@ -414,13 +414,15 @@ __device__ __forceinline__ void g3_block(const Acc<C>& acc, const FfnArgs& p, co
   }
 }
 
-// Plain output of the 256 x 256 tiles through LDS, for outputs no kernel reads
-// soon (streaming stores want whole lines).  Each wave writes two 32-row
-// blocks of its 128 x 64 sub-tile as bf16 into its 8 KB of the idle ring slot
-// (row r keeps 16-byte chunk q at q ^ ((r >> 1) & 7): conflict-free both
-// ways), reads them back eight whole 128-byte rows per instruction and stores
-// those with the non-temporal hint; twice.  Only this wave touches its buffer.
-template <class C>
+// Plain output of the 256 x 256 tiles through LDS, as whole lines.  Each wave
+// writes two 32-row blocks of its 128 x 64 sub-tile as bf16 into its 8 KB of
+// the idle ring slot (row r keeps 16-byte chunk q at q ^ ((r >> 1) & 7):
+// conflict-free both ways), reads them back eight whole 128-byte rows per
+// instruction and stores those; twice.  Only this wave touches its buffer.
+// NT: the non-temporal hint, for outputs no kernel reads soon (the weight
+// gradients); G5's dX rows, read by the dispatch backward right after, keep
+// ordinary stores.
+template <class C, bool NT = true>
 __device__ __forceinline__ void epi_staged_store(const Acc<C>& acc, uint16_t* buf, uint16_t* dst, int64_t ld,
                                                  int rows_valid, int cols_valid, int lane, int wm, int wn) {
   static_assert(C::WTN == 64 && C::TM % 2 == 0, "two 32 x 64 blocks per pass");
@@ -448,7 +450,10 @@ __device__ __forceinline__ void epi_staged_store(const Acc<C>& acc, uint16_t* bu
         const int q = p ^ ((r >> 1) & 7);
         const uint4 v = *reinterpret_cast<const uint4*>(buf + b * 2048 + r * 64 + p * 8);
         const int row = wm * C::WTM + (2 * pass + b) * 32 + r, col = wn * C::WTN + q * 8;
-        if (row < rows_valid && col < cols_valid) store16_nt(dst + row * ld + col, v);
+        if (row < rows_valid && col < cols_valid) {
+          if (NT) store16_nt(dst + row * ld + col, v);
+          else *reinterpret_cast<uint4*>(dst + row * ld + col) = v;
+        }
       }
   }
 }
@@ -676,7 +681,7 @@ void ffn_bf16_kernel(FfnArgs p) {
       __syncthreads();  // the LDS is the ring again
     } else if constexpr (kStagedStore) {
       if (nk > 0) __syncthreads();  // the last step's slot is free
-      epi_staged_store<C>(acc, stage_buf((g + 1) % 2), cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
+      epi_staged_store<C, KIND != kG5>(acc, stage_buf((g + 1) % 2), cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
     } else if constexpr (KIND == kG1) epi_regs_swiglu_fwd<C>(acc, p, cur.row0, cur.rows, cur.n0, lane, wm, wn);
     else if constexpr (KIND == kG3) epi_regs_swiglu_bwd<C>(acc, p, cur.row0, cur.rows, cur.n0, lane, wm, wn);
     else epi_regs_store<C>(acc, cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
