@@ -1,0 +1,62 @@
+"""The measurement script's host-side pieces, on the CPU: the refusal of multi-GPU
+runs, the algorithmic work model behind the roofline figures, and the reading of
+the committed counter summaries."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from mixture_experts_layer_17_amd import workloads as wl  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 5])
+def test_gemm_work_is_eighteen_r_d_f(wid):
+    """Forward 6·R·d·f (gate, up, down) plus backward 12·R·d·f (two products per forward GEMM)."""
+    w = wl.WORKLOADS[wid]
+    total = sum(bench.kernel_work(f"G{i}_x", w, 2)[1] for i in range(1, 7))
+    assert total == 18.0 * w.R * w.d * w.f
+    assert all(bench.kernel_work(f"G{i}_x", w, 2)[0] == "mfma" for i in range(1, 7))
+
+
+def test_data_movement_bytes():
+    w = wl.WORKLOADS[2]
+    T, d, R = w.T, w.d, w.R
+    assert bench.kernel_work("dispatch", w, 2) == ("hbm", float(T * d * 2 + R * d * 2 + 4 * R))
+    assert bench.kernel_work("combine", w, 2) == ("hbm", float(R * d * 2 + T * d * 2 + 8 * R))
+    assert bench.kernel_work("combine_bwd", w, 2) == ("hbm", float(T * d * 2 + 2 * R * d * 2 + 12 * R))
+    # the MXFP8 dispatch also writes one E4M3 byte and 1/32 of a scale byte per element of x_perm
+    w5 = wl.WORKLOADS[5]
+    base = w5.T * w5.d * 2 + w5.R * w5.d * 2 + 4 * w5.R
+    assert bench.kernel_work("dispatch", w5, 2)[1] == pytest.approx(base + w5.R * w5.d * (1 + 1 / 32))
+    assert bench.kernel_work("no_such_kernel", w, 2) == ("other", 0.0)
+
+
+def test_counted_traffic_reads_the_committed_summary():
+    digest = bench.source_digest()
+    assert digest == bench.source_digest() and len(digest) == 16
+    path = os.path.join(ROOT, "profiles", "bf16_e8_T8192_hbm_traffic.md")
+    with open(path) as fh:
+        current = f"source-digest: {digest}" in fh.read()
+    got = bench.counted_traffic("bf16_e8_T8192", "G1_bf16")
+    if not current:
+        assert got is None  # counters taken on other sources are not reported
+        return
+    w = wl.WORKLOADS[2]
+    operands = (w.R * w.d + 2 * w.E * w.d * w.f) * 2  # X_perm and the gate/up weights, read once
+    outputs = 3 * w.R * w.f * 2                      # Hg, Hu, A
+    assert got is not None and got >= operands + outputs
+    assert bench.counted_traffic("no_such_workload", "G1_bf16") is None
+    assert bench.counted_traffic("bf16_e8_T8192", "G9_bf16") is None
