@@ -70,13 +70,17 @@ def topk_select(logits, k):
     the 8->128 benchmark) is chosen per token.  Slot j holds the j-th expert
     under the total order (fp32 logit descending, expert index ascending).
     Values compare as fp32 numbers, so -0.0 and +0.0 tie and the lower index
-    wins.  logits: [T, E] (compared as fp32) -> [T, k] int32.
+    wins.  A NaN logit ranks below every number (-inf included) and NaNs among
+    themselves by index, so the choice is defined for any input (the pages say
+    nothing of non-finite scores; this is the reading taken).
+    logits: [T, E] (compared as fp32) -> [T, k] int32.
     """
     l32 = np.asarray(logits, dtype=np.float32)
     if l32.ndim != 2 or not 1 <= k <= l32.shape[1]:
         raise ValueError("need logits [T, E] and 1 <= k <= E")
     # Negation is exact in fp32; a stable sort keeps ascending expert index
-    # among equal values (and treats -0.0 == +0.0 as equal).
+    # among equal values (and treats -0.0 == +0.0 as equal); numpy's sort puts
+    # NaN after every number, in index order among NaNs.
     order = np.argsort(-l32, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
 

@@ -160,3 +160,57 @@ def test_mx_weight_quantised_along_wrong_axis():
         finally:
             mxl.q_along = inner
     _fails(pins.check_mx_axes, layer_with_bad_axes)
+
+
+def test_mx_recompute_weight_along_wrong_axis(monkeypatch):
+    """The backward's recompute of Hg, Hu with Wg encoded along f instead of d."""
+    from oracle import moe_mx_oracle as mxl
+
+    def bad(X, offsets, w_gate, w_up):
+        E, d, f = np.shape(w_gate)
+        hg, hu = np.zeros((X.shape[0], f)), np.zeros((X.shape[0], f))
+        Xq = mxl.q_along(X, 1)
+        for e in range(E):
+            s = slice(int(offsets[e]), int(offsets[e + 1]))
+            hg[s] = Xq[s] @ mxl.q_along(np.asarray(w_gate[e], np.float64), 1)
+            hu[s] = Xq[s] @ mxl.q_along(np.asarray(w_up[e], np.float64), 0)
+        return hg, hu
+    monkeypatch.setattr(mxl, "mx_expert_ffn_forward_gate_up", bad)
+    _fails(pins.check_mx_recompute, mxl)
+    _fails(pins.check_mx_recompute_axes, mxl)
+
+
+def test_mx_recompute_activation_along_wrong_axis(monkeypatch):
+    """The recompute with X encoded down the tokens instead of along d."""
+    from oracle import moe_mx_oracle as mxl
+    orig = mxl.mx_expert_ffn_forward_gate_up
+
+    def bad(X, offsets, w_gate, w_up):
+        inner = mxl.q_along
+
+        def wrong(v, axis, seg=None):
+            if np.shape(v) == np.shape(X):
+                axis = 1 - axis
+            return inner(v, axis, seg)
+        mxl.q_along = wrong
+        try:
+            return orig(X, offsets, w_gate, w_up)
+        finally:
+            mxl.q_along = inner
+    monkeypatch.setattr(mxl, "mx_expert_ffn_forward_gate_up", bad)
+    _fails(pins.check_mx_recompute, mxl)
+
+
+def test_mx_recompute_skips_silu(monkeypatch):
+    """The fwd=None branch building A without the SiLU (A = Hg * Hu)."""
+    from oracle import moe_mx_oracle as mxl
+    orig_bwd = mxl.mx_expert_ffn_backward
+
+    def bad(dy_perm, x_perm, offsets, w_gate, w_up, w_down, want_dw=True, fwd=None):
+        if fwd is None:
+            hg, hu = mxl.mx_expert_ffn_forward_gate_up(np.asarray(x_perm, np.float64), offsets, w_gate, w_up)
+            fwd = {"h_gate": mxl.round_to_bf16(hg), "h_up": mxl.round_to_bf16(hu),
+                   "a_act": mxl.round_to_bf16(hg * hu)}
+        return orig_bwd(dy_perm, x_perm, offsets, w_gate, w_up, w_down, want_dw=want_dw, fwd=fwd)
+    monkeypatch.setattr(mxl, "mx_expert_ffn_backward", bad)
+    _fails(pins.check_mx_recompute, mxl)

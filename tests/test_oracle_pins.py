@@ -69,7 +69,8 @@ def brute_topk(logits, k):
     out = []
     for row in np.asarray(logits, np.float32):
         vals = [float(v) for v in row]
-        order = sorted(range(len(vals)), key=lambda e: (-vals[e], e))
+        # NaN ranks below every number, NaNs among themselves by index
+        order = sorted(range(len(vals)), key=lambda e: (vals[e] != vals[e], 0.0 if vals[e] != vals[e] else -vals[e], e))
         out.append(order[:k])
     return np.array(out, dtype=np.int32)
 
@@ -84,6 +85,20 @@ def check_topk(topk_fn):
 
 def test_topk_matches_bruteforce():
     check_topk(mo.topk_select)
+
+
+def test_topk_nan_ranks_below_every_number():
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    lg = np.array([[nan, -inf, 0.5, nan, -3.0],
+                   [nan, nan, nan, nan, nan],
+                   [1.0, nan, -inf, nan, 2.0]], np.float32)
+    np.testing.assert_array_equal(mo.topk_select(lg, 4), [[2, 4, 1, 0], [0, 1, 2, 3], [4, 0, 2, 1]])
+    r = np.random.default_rng(5)
+    for E, k in [(8, 4), (16, 8), (5, 5)]:
+        lg = r.standard_normal((200, E)).astype(np.float32)
+        lg[r.random((200, E)) < 0.3] = np.nan
+        lg[r.random((200, E)) < 0.05] = -np.inf
+        np.testing.assert_array_equal(mo.topk_select(lg, k), brute_topk(lg, k))
 
 
 def test_topk_signed_zero_tie_goes_to_lower_index():
@@ -553,3 +568,78 @@ def test_round_to_bf16_matches_torch_conversion():
     ref = torch.from_numpy(v32).to(torch.bfloat16).double().numpy()
     got = mxl.round_to_bf16(v32.astype(np.float64))
     np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 layer oracle: the backward's recompute of the gate/up products
+# ---------------------------------------------------------------------------
+
+def _mx_segments(p):
+    idx = mo.topk_select(p["logits"], p["k"])
+    meta = mo.routing_metadata(idx, p["w_gate"].shape[0])
+    X = mo.dispatch(np.asarray(p["x"], np.float64), meta["perm_src"], p["k"])
+    dy, _ = mo.combine_backward(p["dout"], np.zeros_like(X), mo.topk_gates(p["logits"], idx), meta["perm_dst"],
+                                p["k"])
+    return X, dy, meta["offsets"]
+
+
+def check_mx_recompute(mxl_mod):
+    """The MX backward without saved forward tensors (fwd=None) recomputes Hg, Hu
+    with G1 and must give the bits of the backward fed by the forward's own saved
+    Hg, Hu, A; the recompute (mx_expert_ffn_forward_gate_up) must equal the
+    forward's products before their bf16 store: rounding it gives the forward's
+    stored h_gate, h_up exactly, and with the bf16 store made the identity the
+    forward returns it unchanged.  An empty expert in the middle is included."""
+    p = _mx_problem(seed=29, T=60, d=64, E=5, k=2, f=96)
+    # one expert never chosen: its logit pushed below every other
+    p["logits"] = p["logits"].copy()
+    p["logits"][:, 2] = -1e30
+    X, dy, off = _mx_segments(p)
+    assert off[3] == off[2]
+    wg, wu, wd = p["w_gate"], p["w_up"], p["w_down"]
+    fwd = mxl_mod.mx_expert_ffn_forward(X, off, wg, wu, wd)
+    hg, hu = mxl_mod.mx_expert_ffn_forward_gate_up(X, off, wg, wu)
+    np.testing.assert_array_equal(mxl_mod.round_to_bf16(hg), fwd["h_gate"])
+    np.testing.assert_array_equal(mxl_mod.round_to_bf16(hu), fwd["h_up"])
+    orig = mxl_mod.round_to_bf16
+    mxl_mod.round_to_bf16 = lambda v: np.asarray(v, np.float64)
+    try:
+        raw = mxl_mod.mx_expert_ffn_forward(X, off, wg, wu, wd)
+    finally:
+        mxl_mod.round_to_bf16 = orig
+    np.testing.assert_array_equal(hg, raw["h_gate"])
+    np.testing.assert_array_equal(hu, raw["h_up"])
+    a = mxl_mod.mx_expert_ffn_backward(dy, X, off, wg, wu, wd, fwd=fwd)
+    b = mxl_mod.mx_expert_ffn_backward(dy, X, off, wg, wu, wd, fwd=None)
+    for key in ("dx_perm", "dw_gate", "dw_up", "dw_down"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_mx_backward_recompute_equals_saved_forward():
+    from oracle import moe_mx_oracle as mxl
+    check_mx_recompute(mxl)
+
+
+def check_mx_recompute_axes(mxl_mod):
+    """The recompute encodes X along d and each active expert's Wg, Wu along d,
+    as the forward's G1 does (module table), and nothing else."""
+    p = _mx_problem(T=80, d=64, E=2, k=1, f=96)
+    X, _, off = _mx_segments(p)
+    calls = []
+    orig = mxl_mod.q_along
+
+    def rec(v, axis, seg=None):
+        calls.append((tuple(np.shape(v)), axis, seg is not None))
+        return orig(v, axis, seg)
+    mxl_mod.q_along = rec
+    try:
+        mxl_mod.mx_expert_ffn_forward_gate_up(X, off, p["w_gate"], p["w_up"])
+    finally:
+        mxl_mod.q_along = orig
+    want = [((80, 64), 1, False)] + [((64, 96), 0, False)] * 4
+    assert calls == want, (calls, want)
+
+
+def test_mx_recompute_quantises_along_contraction_axes():
+    from oracle import moe_mx_oracle as mxl
+    check_mx_recompute_axes(mxl)
