@@ -91,9 +91,12 @@ int moe_router_logits_bwd(const void* x, const void* w_r, int dtype, const float
  * of 8 or 128 experts are chosen per token).
  *   logits [T, E] fp32 (input)
  *   topk_idx [T, k] int32: slot j = j-th expert under (logit descending, index
- *            ascending); -0.0 and +0.0 tie
+ *            ascending); -0.0 and +0.0 tie; a NaN logit ranks below every
+ *            number (-inf included), NaNs among themselves by index
  *   gates [T, k] fp32: softmax over the k chosen logits (= softmax over all E,
- *            renormalised over the chosen set)
+ *            renormalised over the chosen set); NaN for every slot of a token
+ *            whose chosen logits include a NaN or whose largest chosen logit
+ *            is infinite (a chosen -inf below a finite largest gets gate 0)
  *   counts [E], offsets [E+1] int32: rows per expert and their exclusive prefix
  *            sum (offsets[E] = R)
  *   perm_src [R] int32: expert-buffer row -> flat slot t*k+j (rows of an expert

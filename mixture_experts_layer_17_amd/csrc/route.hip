@@ -27,6 +27,12 @@ constexpr int kStageBatch = 8;   // 16-byte logit loads per lane in flight while
 constexpr int kScanThreads = 1024;
 constexpr int kScanBatch = 8;    // block counts per thread loaded before any is used
 
+// Order of the selection: a ranks above b when it is larger, or when a is a
+// number and b is NaN (NaN ranks below every number, -inf included); equal
+// values (-0.0 and +0.0 among them) and two NaNs do not rank above each other,
+// so the lower expert index keeps the earlier slot.
+__device__ __forceinline__ bool ranks_above(float a, float b) { return a > b || (b != b && a == a); }
+
 template <int K>
 __global__ __launch_bounds__(64) void route_select_kernel(const float* __restrict__ logits, int64_t T,
                                                           int E, int32_t* __restrict__ topk_idx,
@@ -93,10 +99,10 @@ __global__ __launch_bounds__(64) void route_select_kernel(const float* __restric
     for (int e = 0; e < E; ++e) {
       const float v = row[e];
       // Candidate e has a larger index than every entry held, so it goes in
-      // front of an entry only when strictly greater.  The first K experts
-      // fill the list unconditionally; entries are never duplicated, so the
-      // result is K distinct valid experts for any input (NaN included).
-      const bool take = (e < K) || (v > val[K - 1]);
+      // front of an entry only when it ranks strictly above it.  The first K
+      // experts fill the list unconditionally; entries are never duplicated, so
+      // the result is K distinct valid experts for any input.
+      const bool take = (e < K) || ranks_above(v, val[K - 1]);
       if (take) {
         const int pos = e < K ? e : K - 1;
 #pragma unroll
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(64) void route_select_kernel(const float* __restric
           if (i == pos) { val[i] = v; idx[i] = e; }
 #pragma unroll
         for (int i = K - 1; i >= 1; --i) {
-          if (i <= pos && val[i] > val[i - 1]) {
+          if (i <= pos && ranks_above(val[i], val[i - 1])) {
             const float tv = val[i]; val[i] = val[i - 1]; val[i - 1] = tv;
             const int ti = idx[i]; idx[i] = idx[i - 1]; idx[i - 1] = ti;
           }

@@ -49,6 +49,34 @@ def test_route_topk_bit_exact(gpu, T, E, k, kind):
     assert gu.rel_err(out["gates"].cpu().numpy(), mo.topk_gates(lg, idx)) <= 1e-5
 
 
+@pytest.mark.parametrize("T,E,k", [(300, 8, 4), (1000, 128, 4), (97, 256, 8), (70, 5, 5)])
+def test_route_topk_nan_logits(gpu, T, E, k):
+    """NaN logits rank below every number (-inf included), NaNs among themselves by index: indices and
+    metadata stay bit-exact; gates agree where no NaN was chosen and the largest chosen logit is finite (a
+    chosen -inf then gets gate 0), and are NaN on both sides otherwise."""
+    gu.say(f"case route NaN T={T} E={E} k={k}")
+    r = np.random.default_rng(T + 3 * E)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    lg[r.random((T, E)) < 0.2] = np.nan
+    lg[r.random((T, E)) < 0.03] = -np.inf
+    lg[0] = np.nan                       # every logit NaN
+    lg[1, : E - 1] = np.nan              # a single number
+    out = B.moe_route_topk(torch.from_numpy(lg).cuda(), k)
+    torch.cuda.synchronize()
+    idx = mo.topk_select(lg, k)
+    meta = mo.routing_metadata(idx, E)
+    np.testing.assert_array_equal(out["topk_idx"].cpu().numpy(), idx)
+    for key in ("counts", "offsets", "perm_src", "perm_dst", "mx_blk_offsets"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), meta[key], err_msg=key)
+    chosen = np.take_along_axis(lg, idx.astype(np.int64), axis=1)
+    bad = np.any(np.isnan(chosen), axis=1) | ~np.isfinite(chosen[:, 0])
+    g = out["gates"].cpu().numpy()
+    ref = mo.topk_gates(lg, idx)
+    assert (~bad).sum() > T // 4 and bad.sum() > 0
+    assert gu.rel_err(g[~bad], ref[~bad]) <= 1e-5
+    assert np.all(np.isnan(g[bad])) and np.all(np.isnan(ref[bad]))
+
+
 @pytest.mark.parametrize("T,E,k,bias", [(1000, 8, 4, 0.0), (2048, 128, 4, 3.0), (333, 256, 8, 3.0), (50, 1, 1, 0.0)])
 def test_route_stats_bit_exact(gpu, T, E, k, bias):
     """Load statistics from the device routing equal the oracle's from its own routing (uniform and
