@@ -5,6 +5,7 @@ CPU oracle on the same host inputs.  The two share only the seeded inputs.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -26,14 +27,22 @@ from oracle import moe_oracle as mo
 # E=128 case (~2e-2 per flip), so they get twice that margin.
 TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 2.5e-2}
 TOL_MX_WGRAD = 5e-2
-# The stated bar of the MXFP8 path against the BF16-input (unquantised) oracle.
-MX_VS_BF16_BAR = 6e-2
 INT_KEYS = ("topk_idx", "counts", "offsets", "perm_src", "perm_dst", "mx_blk_offsets")
 
 
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def report(line: str):
+    """Append one line to the parity report named by MOE_PARITY_REPORT (if set), and print it."""
+    say(line)
+    path = os.environ.get("MOE_PARITY_REPORT")
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as fh:
+            fh.write(line + "\n")
 
 
 def rel_err(gpu, ref) -> float:
@@ -82,10 +91,12 @@ def run_oracle(w: wl.Workload, inp: dict, gpu_logits: np.ndarray) -> dict:
                                      logits=gpu_logits.astype(np.float32), w_router=inp.get("w_router"))
 
 
-def check_mx_against_bf16_oracle(w, gpu: dict, mx_ref: dict, inp: dict, keys, rows=None):
-    """Report the MXFP8 path's error against the unquantised oracle next to the
-    error of the exact MX method (the MX oracle) itself, and require the kernels'
-    error to stay within that of the method (plus the bf16 margin)."""
+def check_mx_against_bf16_oracle(w, gpu: dict, mx_ref: dict, inp: dict, keys, rows=None, label=""):
+    """The MXFP8 path's error against the unquantised oracle, next to the error of
+    the exact MX method (the MX oracle) itself; the kernels' error must stay
+    within that of the method plus the bf16 margin.  (The exact method is itself
+    7-16% from the unquantised oracle on these inputs, above the 6e-2 bar the
+    workload text states; the per-tensor pairs go to the parity report.)"""
     bf = mo.layer_forward_backward(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], inp["dout"], w.k,
                                    logits=inp["logits"], want_dw="dw_gate" in keys)
     out = {}
@@ -93,9 +104,10 @@ def check_mx_against_bf16_oracle(w, gpu: dict, mx_ref: dict, inp: dict, keys, ro
         g = gpu[key] if rows is None else gpu[key][rows]
         e_gpu, e_mx = rel_err(g, bf[key]), rel_err(mx_ref[key], bf[key])
         out[key] = (e_gpu, e_mx)
+    report(f"| {w.name} T={w.T} d={w.d} E={w.E} f={w.f}{label} | vs unquantised oracle | " +
+           " ".join(f"{k}=({a:.4f}, {b:.4f})" for k, (a, b) in out.items()) + " |")
+    for key, (e_gpu, e_mx) in out.items():
         assert e_gpu <= 1.25 * e_mx + TOL["bf16"], (key, e_gpu, e_mx)
-    say("  vs unquantised oracle (gpu, exact MX method; bar %.0e): " % MX_VS_BF16_BAR +
-        " ".join(f"{k}=({a:.3f},{b:.3f})" for k, (a, b) in out.items()))
     return out
 
 
@@ -121,8 +133,8 @@ def check_layer(w: wl.Workload, gpu: dict, ref: dict, inp: dict):
         keys.append("dw_router")
     for key in keys:
         errs[key] = rel_err(gpu[key], ref[key])
-    say(f"  {w.name} T={w.T} d={w.d} E={w.E} k={w.k} f={w.f}: " +
-        " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    report(f"| {w.name} T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} | vs oracle ({'MX' if w.prec == 'mxfp8' else 'plain'}) | " +
+           " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + " |")
     bad = {k: v for k, v in errs.items() if v > tol_for(w, k)}
     assert not bad, f"above tolerance: {bad}"
     # empty experts get exactly zero weight gradients
