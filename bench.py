@@ -5,15 +5,21 @@ One step is the whole hot path over one batch: router logits (linear-router
 workloads), top-k routing with device-built metadata, row-wise dispatch, the
 grouped SwiGLU expert FFN forward, the weighted combine, and all their
 backward passes.  Inputs are seeded synthetic tensors already resident in HBM
-when the timed region starts.  Default workload: bf16, T=8192 tokens, d=2048,
-E=8 experts, top-4, expert hidden 1024.
+when the timed region starts.  Default workload: the largest, T=16384 tokens,
+d=4096, E=128 experts, top-4, expert hidden 1536, with MXFP8 expert GEMMs (the
+expert weights quantised to MXFP8 inside every step).
 
 Prints one JSON line.  `value` and `ms_per_step` come from K timed steps as a
-user runs them; the per-kernel times (roofline) come from HIP events the
-library records around each of its launches over a second pass of the same K
-steps (the events cost ~5% of a step, so they stay out of the first pass).  The
-CPU baseline is the fp64 oracle timed on a bounded token sample of the same
-workload.
+user runs them, each bracketed by its own event pair (`step_ms`: median, min,
+max); the per-kernel times (roofline) come from HIP events the library records
+around each of its launches over a second pass of the same K steps (the events
+cost a few percent of a step, so they stay out of the first pass).  With the
+default workload the same line also carries the same shapes and the same bf16
+tensors run with BF16 expert GEMMs (`bf16_same_tensors`, and the MXFP8 / BF16
+rate ratio) and the bf16 E=128 workload at d=2048, f=1024 (`bf16_e128`).  The
+CPU baseline is the fp64 oracle timed on a bounded token sample of the
+headline workload; `cpu_c1_single_core` is the oracle on the tiny fp32 workload
+on one thread (median of 10 runs).
 """
 from __future__ import annotations
 
@@ -141,6 +147,185 @@ def timed_steps(step, steps: int, warmup: int) -> float:
     return a.elapsed_time(b) / steps
 
 
+def host_info() -> dict:
+    """CPU model and the threads this process may use (the oracle's cores)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def smi_sample() -> dict:
+    """Clock and power readings of GPU 0 from amd-smi (a short subprocess; its failure is recorded, not fatal)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True, text=True,
+                           timeout=30)
+    except (OSError, subprocess.SubprocessError) as exc:
+        return {"error": f"{type(exc).__name__}: {exc}"[:200]}
+    if r.returncode != 0:
+        return {"error": (r.stderr or r.stdout).strip()[-200:]}
+    try:
+        data = json.loads(r.stdout)
+    except ValueError:
+        return {"error": "unparsed output", "head": r.stdout[:200]}
+    out = {}
+
+    def walk(node, path):
+        if isinstance(node, dict):
+            for key, val in node.items():
+                walk(val, path + [str(key)])
+        elif isinstance(node, list):
+            for i, val in enumerate(node):
+                walk(val, path + [str(i)])
+        else:
+            key = "/".join(path)
+            low = key.lower()
+            if any(t in low for t in ("gfx_0/clk", "mem_0/clk", "socket_power", "power_limit", "gfx_voltage")) \
+                    and ("value" in low or low.endswith("clk") or "power" in low):
+                out[key] = node
+    walk(data, [])
+    return out or {"raw_head": r.stdout[:600]}
+
+
+def run_workload(w, dev_inp, steps: int, warmup: int, mx_per_step: bool = True) -> dict:
+    """Time one workload: K steps with an event pair around each (value and the per-step spread), then
+    the same K steps with the library's per-launch events (per-kernel durations).  Returns the figures
+    and the LayerStep (for the callers' extra measurements)."""
+    import statistics
+
+    import torch
+
+    from mixture_experts_layer_17_amd import binding as B
+    from mixture_experts_layer_17_amd import layer as L
+
+    step = L.LayerStep(w, dev_inp, mx_weights_per_step=mx_per_step)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    for _ in range(warmup):
+        step.step()
+    torch.cuda.synchronize()
+    print(f"# {w.name}: warm-up done, timing {steps} steps", file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for a, b in ev:
+        a.record()
+        step.step()
+        b.record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / steps
+    per = [a.elapsed_time(b) for a, b in ev]
+
+    # the same K steps with HIP events around every library launch, recorded on the stream the kernels run
+    # on -> per-kernel durations; the events add their own time to this pass only
+    B.moe_timing_enable(True)
+    step.step()
+    torch.cuda.synchronize()
+    B.moe_timing_report()  # discard the warm-up records (the event pool is now warm)
+    start.record()
+    for _ in range(steps):
+        step.step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_instrumented = start.elapsed_time(stop) / steps
+    kern = B.moe_timing_report()
+    B.moe_timing_enable(False)
+    peak_mem = torch.cuda.max_memory_allocated()
+    s = 4 if w.storage == "f32" else 2
+    per_step_us = {name: 1e3 * ms / steps for name, (n, ms) in kern.items()}
+    per_launch_us = {name: 1e3 * ms / n for name, (n, ms) in kern.items()}
+    gemm_us = sum(v for kname, v in per_step_us.items() if kname[:2] in ("G1", "G2", "G3", "G4", "G5", "G6"))
+    gemm_flops = 18.0 * w.R * w.d * w.f
+    gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12 if gemm_us > 0 else None
+    memk = {}
+    for name in ("dispatch", "combine", "combine_bwd", "dispatch_bwd"):
+        if name in per_launch_us:
+            _, b = kernel_work(name, w, s)
+            memk[name] = round(b / (per_launch_us[name] * 1e-6) / 1e9, 1)
+    return {
+        "step": step, "ms_per_step": ms_per_step, "per_step_ms": per, "ms_instrumented": ms_instrumented,
+        "per_step_us": per_step_us, "per_launch_us": per_launch_us, "gemm_us": gemm_us, "gemm_flops": gemm_flops,
+        "gemm_tflops": gemm_tflops, "memk": memk, "peak_mem": peak_mem, "s": s,
+        "spread": {"median_ms": statistics.median(per), "min_ms": min(per), "max_ms": max(per)},
+    }
+
+
+def roofline(w, r: dict) -> dict:
+    """The dominant kernel (largest time per step) against its roof, with its counted traffic if committed."""
+    per_step_us, per_launch_us = r["per_step_us"], r["per_launch_us"]
+    dom = max(per_step_us, key=per_step_us.get)
+    bound, work = kernel_work(dom, w, r["s"])
+    avg_s = per_launch_us[dom] * 1e-6
+    tag = f"{w.name.replace('-', '_')}_T{w.T}"
+    traffic = counted_traffic(tag, dom)
+    if bound == "mfma":
+        peak = PEAK[w.prec]
+        roof = {"bound": "mfma" if w.prec != "f32" else "alu", "kernel": dom, "achieved": work / avg_s / 1e12,
+                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": work / avg_s / peak, "traffic": traffic,
+                "work_per_launch": f"{work:.4g} FLOP", "avg_launch_us": per_launch_us[dom]}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": work / avg_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": work / avg_s / HBM_PEAK, "traffic": traffic,
+                "work_per_launch": f"{work:.4g} B", "avg_launch_us": per_launch_us[dom]}
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, copy-calibrated)"
+    roof["traffic_source"] = f"profiles/{tag}_hbm_traffic.md" if traffic is not None else \
+        "null: no counter summary taken with the current kernel sources"
+    return roof
+
+
+def summary(w, r: dict) -> dict:
+    """Compact figures of one workload for the JSON line."""
+    peak = PEAK[w.prec]
+    return {
+        "workload": f"{w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f}, {w.prec} expert GEMMs",
+        "tokens_per_s": w.T / (r["ms_per_step"] * 1e-3), "ms_per_step": r["ms_per_step"],
+        "step_ms": r["spread"],
+        "gemm": {"tflops": r["gemm_tflops"], "frac_of_peak": (r["gemm_tflops"] * 1e12 / peak) if r["gemm_tflops"]
+                 else None, "peak_tflops": peak / 1e12, "us_per_step": r["gemm_us"]},
+        "hbm_kernels_gbps": r["memk"],
+        "roofline": roofline(w, r),
+        "kernels_us_per_step": {k: round(v, 2) for k, v in sorted(r["per_step_us"].items())},
+        "peak_mem_gib": r["peak_mem"] / 2**30,
+    }
+
+
+def c1_single_core(runs: int = 10) -> dict:
+    """The oracle on the tiny fp32 workload on one thread: median of `runs` runs."""
+    import statistics
+
+    from threadpoolctl import threadpool_limits
+
+    from mixture_experts_layer_17_amd import workloads as wl
+    from oracle import moe_oracle as mo
+
+    w = wl.WORKLOADS[1]
+    inp = wl.make_inputs(w)
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            mo.layer_forward_backward(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], inp["dout"], w.k,
+                                      w_router=inp["w_router"])
+            times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f}", "median_s": med,
+            "min_s": min(times), "runs": runs, "tokens_per_s": w.T / med, "cores": 1}
+
+
 def pool_sweep(args) -> int:
     """Expert-pool sweep at a fixed token count: how the layer's throughput moves as the same routed rows
     spread over more, smaller experts (the pages report a small drop from 8 to 128 experts at top-4)."""
@@ -177,9 +362,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: bf16, E=8, top-4)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1..5 (default 5: MXFP8, T=16384, d=4096, E=128, top-4, f=1536, the largest)")
     ap.add_argument("--seed", type=int, default=17)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="with workload 5: skip the BF16 run on the same tensors and the bf16-e128 workload")
     ap.add_argument("--trace-only", action="store_true",
                     help="only the warm-up and the timed steps (for profiler traces: every launch belongs to a "
                          "step), then a short JSON line")
@@ -191,6 +379,11 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the MoE layer; the library has no multi-GPU path "
+              "(no collectives, no expert sharding), so only --gpus 1 runs.", file=sys.stderr)
+        return 2
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20
@@ -201,11 +394,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
         return 0
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the MoE layer; the library has no multi-GPU path "
-              "(no collectives, no expert sharding), so only --gpus 1 runs.", file=sys.stderr)
-        return 2
+
+    import dataclasses
 
     import torch
 
@@ -221,102 +411,47 @@ def main() -> int:
     w = wl.WORKLOADS[args.workload]
     print(f"# workload {w.name} {w.describe()}: generating inputs", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed=args.seed)
-    # MXFP8: each step quantises the expert weights once, into both layouts, for its forward and backward
-    step = L.LayerStep(w, L.to_device(inp), mx_weights_per_step=True)
-    torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats()
-
-    for _ in range(args.warmup):
-        step.step()
-    torch.cuda.synchronize()
-    print(f"# warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
-
-    # timed region 1: the step as a user runs it (no per-launch instrumentation) -> value, ms_per_step
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step.step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
+    dev_inp = L.to_device(inp)
     if args.trace_only:
-        print(json.dumps({"metric": METRIC, "value": w.T / (ms_per_step * 1e-3), "unit": "tokens/s",
-                          "ms_per_step": ms_per_step, "steps": args.steps, "warmup": args.warmup,
+        # MXFP8: each step quantises the expert weights once, into both layouts, for its forward and backward
+        step = L.LayerStep(w, dev_inp, mx_weights_per_step=True)
+        ms = timed_steps(step, args.steps, args.warmup)
+        print(json.dumps({"metric": METRIC, "value": w.T / (ms * 1e-3), "unit": "tokens/s",
+                          "ms_per_step": ms, "steps": args.steps, "warmup": args.warmup,
                           "workload": w.name, "trace_only": True}), flush=True)
         return 0
-
-    # timed region 2: the same K steps with HIP events around every library launch, recorded on the stream the
-    # kernels run on -> per-kernel durations (roofline); the events add their own time to this pass only
-    B.moe_timing_enable(True)
-    step.step()
-    torch.cuda.synchronize()
-    B.moe_timing_report()  # discard the warm-up records (the event pool is now warm)
-    start.record()
-    for _ in range(args.steps):
-        step.step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_instrumented = start.elapsed_time(stop) / args.steps
-    kern = B.moe_timing_report()
-    B.moe_timing_enable(False)
-    peak_mem = torch.cuda.max_memory_allocated()
+    smi_before = smi_sample()
+    # the headline workload; MXFP8 steps quantise the expert weights once per step into both layouts
+    r = run_workload(w, dev_inp, args.steps, args.warmup, mx_per_step=True)
+    step = r["step"]
     rs = B.moe_route_stats(step.route["counts"]).cpu().tolist()  # after the timed region
-
-    s = 4 if w.storage == "f32" else 2
-    per_step_us = {name: 1e3 * ms / args.steps for name, (n, ms) in kern.items()}
-    per_launch_us = {name: 1e3 * ms / n for name, (n, ms) in kern.items()}
-    gemm_us = sum(v for kname, v in per_step_us.items() if kname[:2] in ("G1", "G2", "G3", "G4", "G5", "G6"))
-    gemm_flops = 18.0 * w.R * w.d * w.f
-    gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12 if gemm_us > 0 else None
-    dom = max(per_step_us, key=per_step_us.get)
-    bound, work = kernel_work(dom, w, s)
-    avg_s = per_launch_us[dom] * 1e-6
-    tag = f"{w.name.replace('-', '_')}_T{w.T}"
-    traffic = counted_traffic(tag, dom)
-    if bound == "mfma":
-        peak = PEAK[w.prec]
-        roof = {"bound": "mfma" if w.prec != "f32" else "alu", "kernel": dom, "achieved": work / avg_s / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": work / avg_s / peak, "traffic": traffic,
-                "work_per_launch": f"{work:.4g} FLOP", "avg_launch_us": per_launch_us[dom]}
-    else:
-        roof = {"bound": "hbm", "kernel": dom, "achieved": work / avg_s / 1e9, "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": work / avg_s / HBM_PEAK, "traffic": traffic,
-                "work_per_launch": f"{work:.4g} B", "avg_launch_us": per_launch_us[dom]}
-    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, copy-calibrated)"
-    roof["traffic_source"] = f"profiles/{tag}_hbm_traffic.md" if traffic is not None else \
-        "null: no counter summary taken with the current kernel sources"
-    memk = {}
-    for name in ("dispatch", "combine", "combine_bwd", "dispatch_bwd"):
-        if name in per_launch_us:
-            _, b = kernel_work(name, w, s)
-            memk[name] = round(b / (per_launch_us[name] * 1e-6) / 1e9, 1)
-
+    head = summary(w, r)
     line = {
         "metric": METRIC,
-        "value": w.T / (ms_per_step * 1e-3),
+        "value": w.T / (r["ms_per_step"] * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8"}[w.prec],
         "data": "synthetic: seeded normal activations/logits/upstream grads, random-init weights (std 0.02)",
         "config": {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f}, SwiGLU experts, "
-                               f"fwd+bwd incl. routing", "global_batch": w.T, "parallelism": "single GPU"},
-        "roofline": roof,
-        "gemm": {"tflops": gemm_tflops, "frac_of_peak": (gemm_tflops * 1e12 / PEAK[w.prec]) if gemm_tflops else None,
-                 "flops_per_step": gemm_flops, "us_per_step": gemm_us},
-        "hbm_kernels_gbps": memk,
-        "kernels_us_per_step": {k: round(v, 2) for k, v in sorted(per_step_us.items())},
+                               f"fwd+bwd incl. routing" + (", expert weights quantised to MXFP8 every step"
+                                                          if w.prec == "mxfp8" else ""),
+                   "global_batch": w.T, "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "step_ms": head["step_ms"],
+        "gemm": head["gemm"],
+        "hbm_kernels_gbps": head["hbm_kernels_gbps"],
+        "kernels_us_per_step": head["kernels_us_per_step"],
         "kernel_timing": f"HIP events around every launch over a second pass of the same {args.steps} steps "
-                         f"({ms_instrumented:.3f} ms/step with the events; value and ms_per_step come from the "
-                         f"first pass, without them)",
-        "peak_mem_gib": peak_mem / 2**30,
+                         f"({r['ms_instrumented']:.3f} ms/step with the events; value, ms_per_step and step_ms "
+                         f"come from the first pass, one event pair per step)",
+        "peak_mem_gib": head["peak_mem_gib"],
         "routing_stats": {"max_rows": rs[0], "min_rows": rs[1], "empty_experts": rs[2], "rows": rs[3],
                           "max_over_mean": rs[0] * w.E / max(rs[3], 1)},
     }
@@ -342,9 +477,30 @@ def main() -> int:
             "once": {"tokens_per_s": w.T / (ms_once * 1e-3), "ms_per_step": ms_once,
                      "note": "weights quantised once before the loop and reused (build excluded): the rate of "
                              "micro-batches that share one optimiser step"}}
+    del step, r
+    torch.cuda.empty_cache()
+    if w.prec == "mxfp8" and not args.no_companions:
+        # the same shapes and the same bf16 tensors with BF16 expert GEMMs: the MXFP8 / BF16 comparison
+        wb = dataclasses.replace(w, name=f"{w.name}-as-bf16", prec="bf16")
+        print(f"# {wb.name}: same tensors, BF16 expert GEMMs", file=sys.stderr, flush=True)
+        rb = run_workload(wb, dev_inp, args.steps, args.warmup)
+        line["bf16_same_tensors"] = summary(wb, rb)
+        line["mxfp8_over_bf16"] = line["value"] / line["bf16_same_tensors"]["tokens_per_s"]
+        del rb
+        torch.cuda.empty_cache()
+        w3 = wl.WORKLOADS[3]
+        print(f"# workload {w3.name}: generating inputs", file=sys.stderr, flush=True)
+        d3 = L.to_device(wl.make_inputs(w3, seed=args.seed))
+        r3 = run_workload(w3, d3, args.steps, args.warmup)
+        line["bf16_e128"] = summary(w3, r3)
+        del r3, d3
+        torch.cuda.empty_cache()
+    line["gpu_clocks_power"] = {"before": smi_before, "after": smi_sample()}
+    line["host"] = host_info()
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        line["cpu_c1_single_core"] = c1_single_core()
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
