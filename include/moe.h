@@ -111,6 +111,21 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
                    int32_t* perm_dst, int32_t* mx_blk_offsets, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* moe_route_topk without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs and bits as moe_route_topk;
+ * the scratch is a static 8 MiB device array that the library holds on each
+ * GPU it runs on until the process ends (the current device's copy is used:
+ * the stream must belong to the current device).  Limits: T*k <= 2^20 and
+ * ceil(T/64)*E <= 2^20, else MOE_EWORKSPACE with nothing launched; MOE_EHIP
+ * if the array's device address cannot be obtained.  Every byte of the scratch
+ * is written before it is read, so nothing needs clearing between calls, but
+ * all calls on one GPU share it: calls that overlap on one GPU (different
+ * streams, or host threads) race and give undefined results. */
+int moe_route_topk_noalloc(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                           float* gates, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                           int32_t* perm_dst, int32_t* mx_blk_offsets, void* stream);
+
 /* Backward of the renormalised gates: dlogits[t, S_j] = g_j (dg_j - sum_i g_i dg_i),
  * zero for unselected experts.  gates, dgates [T, k] fp32, topk_idx [T, k];
  * dlogits [T, E] fp32, overwritten. */

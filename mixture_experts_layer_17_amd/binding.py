@@ -32,6 +32,7 @@ _SIGS = {
                                      _c_void_p, _c_void_p, _sz, _c_void_p]),
     "moe_route_topk_workspace": (_sz, [_i64, _i32, _i32]),
     "moe_route_topk": (_int, [_c_void_p, _i64, _i32, _i32] + [_c_void_p] * 8 + [_sz, _c_void_p]),
+    "moe_route_topk_noalloc": (_int, [_c_void_p, _i64, _i32, _i32] + [_c_void_p] * 8),
     "moe_route_topk_bwd": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_dispatch": (_int, [_c_void_p, _int, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "moe_dispatch_bwd": (_int, [_c_void_p, _int, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
@@ -148,6 +149,16 @@ def moe_route_topk(logits, k, out=None, ws=None):
     _check(lib().moe_route_topk(_p(logits), T, E, k, _p(out["topk_idx"]), _p(out["gates"]), _p(out["counts"]),
                                 _p(out["offsets"]), _p(out["perm_src"]), _p(out["perm_dst"]),
                                 _p(out.get("mx_blk_offsets")), _p(ws), ws.numel(), _stream()), "moe_route_topk")
+    return out
+
+
+def moe_route_topk_noalloc(logits, k, out):
+    """moe_route_topk on the library's static scratch (no workspace); `out` as moe_route_topk returns it."""
+    T, E = logits.shape
+    _check(lib().moe_route_topk_noalloc(_p(logits), T, E, k, _p(out["topk_idx"]), _p(out["gates"]),
+                                        _p(out["counts"]), _p(out["offsets"]), _p(out["perm_src"]),
+                                        _p(out["perm_dst"]), _p(out.get("mx_blk_offsets")), _stream()),
+           "moe_route_topk_noalloc")
     return out
 
 

@@ -16,6 +16,8 @@
 //  2. route_scan: one workgroup turns the [blocks x E] count matrix into
 //     counts, offsets, MX block offsets and per-(block, expert) base rows.
 //  3. route_scatter: row = base[block][e] + rank; writes perm_dst and perm_src.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -340,15 +342,23 @@ extern "C" size_t moe_route_topk_workspace(int64_t T, int32_t E, int32_t k) {
   return route_ws_bytes(T, E, k);
 }
 
-extern "C" int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
-                              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                              int32_t* perm_dst, int32_t* mx_blk_offsets, void* ws, size_t ws_bytes,
-                              void* stream) {
+namespace moe {
+namespace {
+
+// Validation shared by moe_route_topk and moe_route_topk_noalloc (everything but the workspace).
+int route_check(const float* logits, int64_t T, int E, int k, const int32_t* topk_idx, const float* gates,
+                const int32_t* counts, const int32_t* offsets, const int32_t* perm_src, const int32_t* perm_dst) {
   if (!route_args_ok(T, E, k)) return (E > kMaxE || k > kMaxK) ? MOE_EUNSUPPORTED : MOE_EINVAL;
-  if (!counts || !offsets || !ws) return MOE_EINVAL;
+  if (!counts || !offsets) return MOE_EINVAL;
   if (T > 0 && (!logits || !topk_idx || !gates || !perm_src || !perm_dst)) return MOE_EINVAL;
-  if (ws_bytes < route_ws_bytes(T, E, k)) return MOE_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// The three routing launches over a scratch area of route_ws_bytes(T, E, k)
+// bytes at ws (every byte of it is written before it is read).
+int route_launch(const float* logits, int64_t T, int E, int k, int32_t* topk_idx, float* gates, int32_t* counts,
+                 int32_t* offsets, int32_t* perm_src, int32_t* perm_dst, int32_t* mx_blk_offsets, void* ws,
+                 hipStream_t s) {
   const int64_t nblk = cdiv(T, kTokPerBlk);
   int32_t* rank = static_cast<int32_t*>(ws);
   int32_t* blk = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(static_cast<size_t>(T * k) * 4, 256));
@@ -372,6 +382,63 @@ extern "C" int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t
                        topk_idx, rank, blk, R, k, E, perm_src, perm_dst);
   }
   return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Routing without allocation (moe_route_topk_noalloc): the same launches with
+// their scratch in a static device array of kNoAllocBytes per GPU, which each
+// GPU the library runs on holds until the process ends.  Limits: T*k and
+// ceil(T/64)*E at most 2^20 each, so route_ws_bytes <= 4 MiB + 4 MiB.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoAllocRows = int64_t{1} << 20;
+constexpr int64_t kNoAllocBlkCounts = int64_t{1} << 20;
+constexpr size_t kNoAllocBytes = static_cast<size_t>(kNoAllocRows + kNoAllocBlkCounts) * 4;
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// with hipGetSymbolAddress (in host code the array's name is only a stand-in).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* perm_dst, int32_t* mx_blk_offsets, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const int st = route_check(logits, T, E, k, topk_idx, gates, counts, offsets, perm_src, perm_dst);
+  if (st != MOE_OK) return st;
+  if (!ws) return MOE_EINVAL;
+  if (ws_bytes < route_ws_bytes(T, E, k)) return MOE_EWORKSPACE;
+  return route_launch(logits, T, E, k, topk_idx, gates, counts, offsets, perm_src, perm_dst, mx_blk_offsets, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" int moe_route_topk_noalloc(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                                      float* gates, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                      int32_t* perm_dst, int32_t* mx_blk_offsets, void* stream) {
+  const int st = route_check(logits, T, E, k, topk_idx, gates, counts, offsets, perm_src, perm_dst);
+  if (st != MOE_OK) return st;
+  if (T * k > kNoAllocRows || cdiv(T, kTokPerBlk) * E > kNoAllocBlkCounts) return MOE_EWORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return MOE_EHIP;
+  return route_launch(logits, T, E, k, topk_idx, gates, counts, offsets, perm_src, perm_dst, mx_blk_offsets, ws,
+                      static_cast<hipStream_t>(stream));
 }
 
 extern "C" int moe_route_topk_bwd(const float* gates, const float* dgates, const int32_t* topk_idx,

@@ -124,3 +124,13 @@ def test_permute_and_quantiser_validation(L):
     assert L.mx_quantize(FAKE, 1, 1, 40, 64, 0, None, 0, FAKE, FAKE, s) == EINVAL     # rows % 32
     assert L.mx_quantize(FAKE, 1, 2, 40, 64, 0, FAKE, 3, FAKE, FAKE, s) == EINVAL     # segments need batch 1
     assert L.moe_router_logits(FAKE, FAKE, 1, 10, 64, 300, FAKE, s) == EINVAL         # E > 256
+
+
+def test_route_topk_noalloc_validation(L):
+    """Sizes past the static scratch and bad arguments are refused on the host, before any GPU call."""
+    s = None
+    assert L.moe_route_topk_noalloc(FAKE, (1 << 20) // 4 + 1, 8, 4, *[FAKE] * 7, s) == EWS   # T*k > 2^20
+    assert L.moe_route_topk_noalloc(FAKE, 64 * 4097, 256, 1, *[FAKE] * 7, s) == EWS          # blocks*E > 2^20
+    assert L.moe_route_topk_noalloc(FAKE, 10, 4, 5, *[FAKE] * 7, s) == EINVAL                # k > E
+    assert L.moe_route_topk_noalloc(None, 10, 8, 2, *[FAKE] * 7, s) == EINVAL                # null logits
+
