@@ -126,9 +126,14 @@ int moe_route_topk_noalloc(const float* logits, int64_t T, int32_t E, int32_t k,
                            float* gates, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                            int32_t* perm_dst, int32_t* mx_blk_offsets, void* stream);
 
-/* Backward of the renormalised gates: dlogits[t, S_j] = g_j (dg_j - sum_i g_i dg_i),
- * zero for unselected experts.  gates, dgates [T, k] fp32, topk_idx [T, k];
- * dlogits [T, E] fp32, overwritten. */
+/* Backward of the renormalised gates (the router is trained with the rest of
+ * the layer in the MoE training path of "Scaling and optimizing MoE training";
+ * the pages give no gradient formula, so this is the exact gradient of the
+ * gates moe_route_topk computes): dlogits[t, S_j] = g_j (dg_j - sum_i g_i dg_i),
+ * exactly zero for unselected experts (the renormalised gates do not depend on
+ * them).  gates, dgates [T, k] fp32, topk_idx [T, k] from moe_route_topk;
+ * dlogits [T, E] fp32, overwritten.  MOE_EINVAL / MOE_EUNSUPPORTED for bad
+ * sizes or null pointers, nothing launched; T = 0 is a no-op. */
 int moe_route_topk_bwd(const float* gates, const float* dgates, const int32_t* topk_idx, int64_t T,
                        int32_t E, int32_t k, float* dlogits, void* stream);
 

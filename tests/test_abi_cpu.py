@@ -134,3 +134,17 @@ def test_route_topk_noalloc_validation(L):
     assert L.moe_route_topk_noalloc(FAKE, 10, 4, 5, *[FAKE] * 7, s) == EINVAL                # k > E
     assert L.moe_route_topk_noalloc(None, 10, 8, 2, *[FAKE] * 7, s) == EINVAL                # null logits
 
+
+# The entry points of the boundary as first drafted (names only; the header documents where the signatures
+# depart from that draft, and why).
+DRAFT_CALLS = ["moe_abi_version", "moe_status_str", "moe_route_topk_workspace", "moe_route_topk",
+               "moe_route_topk_bwd", "moe_router_logits", "moe_router_logits_bwd", "moe_dispatch", "moe_dispatch_bwd",
+               "moe_combine", "moe_combine_bwd", "moe_grouped_ffn_workspace", "moe_grouped_ffn_fwd",
+               "moe_grouped_ffn_bwd", "mx_quantize"]
+
+
+def test_every_drafted_call_is_declared_and_exported(L):
+    decl = declared_functions()
+    for name in DRAFT_CALLS:
+        assert name in decl, name
+        assert hasattr(L, name), name
