@@ -107,6 +107,25 @@ def kernel_work(name: str, w, s: int) -> tuple[str, float]:
     return "other", 0.0
 
 
+def gemm_bytes(name: str, w, active: int) -> float:
+    """Algorithmic HBM bytes of one grouped-GEMM launch: every operand read once and every output written once.
+    Operands are bf16 (2 bytes), or for the MXFP8 GEMMs their E4M3 codes plus one E8M0 byte per 32; the saved
+    bf16 Hg, Hu read by G3's SwiGLU backward and every output are bf16.  Row-grouped GEMMs read the weights of the
+    `active` experts (those with rows); the weight gradients write all E experts' dW."""
+    T, d, E, k, f, R = w.T, w.d, w.E, w.k, w.f, w.R
+    o = (1 + 1 / 32) if w.prec == "mxfp8" else (4 if w.storage == "f32" else 2)
+    b = 4 if w.storage == "f32" else 2
+    g = name.split("_")[0]
+    return float({
+        "G1": R * d * o + 2 * active * d * f * o + 3 * R * f * b,
+        "G2": R * f * o + active * f * d * o + R * d * b,
+        "G3": R * d * o + active * f * d * o + 2 * R * f * b + 2 * R * f * b,
+        "G4": R * f * o + R * d * o + E * f * d * b,
+        "G5": 2 * R * f * o + 2 * active * d * f * o + R * d * b,
+        "G6": R * d * o + 2 * R * f * o + 2 * E * d * f * b,
+    }[g])
+
+
 def cpu_baseline(w, inp, target_s: float) -> dict:
     """The oracle, untuned, on a bounded token sample of the same workload."""
     import numpy as np
@@ -264,11 +283,17 @@ def run_workload(w, dev_inp, steps: int, warmup: int, mx_per_step: bool = True) 
     }
 
 
-def roofline(w, r: dict) -> dict:
-    """The dominant kernel (largest time per step) against its roof, with its counted traffic if committed."""
+def roofline(w, r: dict, active: int) -> dict:
+    """The dominant kernel (largest time per step) against its binding roof, with its counted traffic if committed.
+    A grouped GEMM is bound by whichever takes longer at peak: its FLOPs on the matrix cores or its algorithmic
+    bytes over HBM."""
     per_step_us, per_launch_us = r["per_step_us"], r["per_launch_us"]
     dom = max(per_step_us, key=per_step_us.get)
     bound, work = kernel_work(dom, w, r["s"])
+    if bound == "mfma" and w.prec != "f32":
+        nbytes = gemm_bytes(dom, w, active)
+        if nbytes / HBM_PEAK > work / PEAK[w.prec]:
+            bound, work = "hbm", nbytes
     avg_s = per_launch_us[dom] * 1e-6
     tag = f"{w.name.replace('-', '_')}_T{w.T}"
     traffic = counted_traffic(tag, dom)
@@ -287,7 +312,23 @@ def roofline(w, r: dict) -> dict:
     return roof
 
 
-def summary(w, r: dict) -> dict:
+def gemm_roofs(w, r: dict, active: int) -> dict:
+    """Each grouped GEMM against its binding roof (matrix cores or HBM, whichever takes longer at peak)."""
+    out = {}
+    for name, us in sorted(r["per_launch_us"].items()):
+        bound, flops = kernel_work(name, w, r["s"])
+        if bound != "mfma" or w.prec == "f32":
+            continue
+        nbytes = gemm_bytes(name, w, active)
+        t_mfma, t_hbm = flops / PEAK[w.prec], nbytes / HBM_PEAK
+        out[name] = {"us": round(us, 1), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                     "frac_mfma": round(t_mfma / (us * 1e-6), 3), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(t_hbm / (us * 1e-6), 3), "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                     "frac_roof": round(max(t_mfma, t_hbm) / (us * 1e-6), 3)}
+    return out
+
+
+def summary(w, r: dict, active: int) -> dict:
     """Compact figures of one workload for the JSON line."""
     peak = PEAK[w.prec]
     return {
@@ -297,7 +338,8 @@ def summary(w, r: dict) -> dict:
         "gemm": {"tflops": r["gemm_tflops"], "frac_of_peak": (r["gemm_tflops"] * 1e12 / peak) if r["gemm_tflops"]
                  else None, "peak_tflops": peak / 1e12, "us_per_step": r["gemm_us"]},
         "hbm_kernels_gbps": r["memk"],
-        "roofline": roofline(w, r),
+        "roofline": roofline(w, r, active),
+        "gemm_roofs": gemm_roofs(w, r, active),
         "kernels_us_per_step": {k: round(v, 2) for k, v in sorted(r["per_step_us"].items())},
         "peak_mem_gib": r["peak_mem"] / 2**30,
     }
@@ -425,7 +467,7 @@ def main() -> int:
     r = run_workload(w, dev_inp, args.steps, args.warmup, mx_per_step=True)
     step = r["step"]
     rs = B.moe_route_stats(step.route["counts"]).cpu().tolist()  # after the timed region
-    head = summary(w, r)
+    head = summary(w, r, w.E - rs[2])
     line = {
         "metric": METRIC,
         "value": w.T / (r["ms_per_step"] * 1e-3),
@@ -446,6 +488,7 @@ def main() -> int:
         "roofline": head["roofline"],
         "step_ms": head["step_ms"],
         "gemm": head["gemm"],
+        "gemm_roofs": head["gemm_roofs"],
         "hbm_kernels_gbps": head["hbm_kernels_gbps"],
         "kernels_us_per_step": head["kernels_us_per_step"],
         "kernel_timing": f"HIP events around every launch over a second pass of the same {args.steps} steps "
@@ -484,7 +527,7 @@ def main() -> int:
         wb = dataclasses.replace(w, name=f"{w.name}-as-bf16", prec="bf16")
         print(f"# {wb.name}: same tensors, BF16 expert GEMMs", file=sys.stderr, flush=True)
         rb = run_workload(wb, dev_inp, args.steps, args.warmup)
-        line["bf16_same_tensors"] = summary(wb, rb)
+        line["bf16_same_tensors"] = summary(wb, rb, w.E - rs[2])
         line["mxfp8_over_bf16"] = line["value"] / line["bf16_same_tensors"]["tokens_per_s"]
         del rb
         torch.cuda.empty_cache()
@@ -492,7 +535,8 @@ def main() -> int:
         print(f"# workload {w3.name}: generating inputs", file=sys.stderr, flush=True)
         d3 = L.to_device(wl.make_inputs(w3, seed=args.seed))
         r3 = run_workload(w3, d3, args.steps, args.warmup)
-        line["bf16_e128"] = summary(w3, r3)
+        rs3 = B.moe_route_stats(r3["step"].route["counts"]).cpu().tolist()
+        line["bf16_e128"] = summary(w3, r3, w3.E - rs3[2])
         del r3, d3
         torch.cuda.empty_cache()
     line["gpu_clocks_power"] = {"before": smi_before, "after": smi_sample()}

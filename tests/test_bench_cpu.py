@@ -60,3 +60,23 @@ def test_counted_traffic_reads_the_committed_summary():
     assert got is not None and got >= operands + outputs
     assert bench.counted_traffic("no_such_workload", "G1_bf16") is None
     assert bench.counted_traffic("bf16_e8_T8192", "G9_bf16") is None
+
+
+def test_gemm_bytes_and_binding_roof():
+    """Algorithmic bytes per GEMM launch: operands read once, outputs written once; the MXFP8 weight gradients
+    (bf16 dW of all 128 experts written) are bound by HBM, the forward gate/up GEMM by the matrix cores."""
+    w5 = wl.WORKLOADS[5]
+    R, d, f, E = w5.R, w5.d, w5.f, w5.E
+    o = 1 + 1 / 32
+    assert bench.gemm_bytes("G6_mx", w5, E) == pytest.approx(R * d * o + 2 * R * f * o + 2 * E * d * f * 2)
+    assert bench.gemm_bytes("G1_mx", w5, 64) == pytest.approx(R * d * o + 2 * 64 * d * f * o + 3 * R * f * 2)
+    r = {"per_step_us": {"G6_mx": 1000.0, "G1_mx": 900.0}, "per_launch_us": {"G6_mx": 1000.0, "G1_mx": 900.0},
+         "s": 2}
+    roof = bench.roofline(w5, r, E)
+    assert roof["kernel"] == "G6_mx" and roof["bound"] == "hbm" and roof["unit"] == "GB/s"
+    assert roof["achieved"] == pytest.approx(bench.gemm_bytes("G6_mx", w5, E) / 1e-3 / 1e9)
+    roofs = bench.gemm_roofs(w5, r, E)
+    assert roofs["G1_mx"]["bound"] == "mfma" and roofs["G6_mx"]["bound"] == "hbm"
+    w2 = wl.WORKLOADS[2]  # bf16, E = 8: every GEMM bound by the matrix cores
+    r2 = {"per_step_us": {"G1_bf16": 300.0}, "per_launch_us": {"G1_bf16": 300.0}, "s": 2}
+    assert bench.roofline(w2, r2, 8)["bound"] == "mfma"
