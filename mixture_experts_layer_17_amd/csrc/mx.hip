@@ -114,7 +114,8 @@ constexpr int kColW = 64;
 // qr [batch, rows, cols], scr [batch, rows, cols/32] (one read of the source
 // serves both orientations).
 template <typename T, bool BOTH, bool GROUPED>
-__global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+__global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src, int64_t batch, int64_t rows,
+                                                     int64_t cols,
                                                      const int32_t* __restrict__ seg, const int32_t* __restrict__ blk,
                                                      int nseg, int64_t ldq,
                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
@@ -135,9 +136,26 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
   __shared__ int64_t b_r0[4];
   __shared__ int b_nv[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t bz = blockIdx.z;
+  // Tile of this workgroup.  BOTH: the two 64-column tiles of each 128-column
+  // span go to workgroups 8 ids apart, hence on the same XCD, so the two
+  // 64-byte halves of each row-layout line meet in one L2 (consecutive ids
+  // alternate over the 8 XCDs); the grid is flat, 16 ids per 8 spans.
+  int64_t bx, by, bz;
+  if constexpr (BOTH) {
+    const int64_t gx = (cols + kColW - 1) / kColW, gy = (rows / 32 + 3) / 4;
+    const int64_t L = blockIdx.x, P = (L >> 4) * 8 + (L & 7), half = (L >> 3) & 1;
+    const int64_t spans = gx / 2;  // cols % 128 == 0
+    bx = 2 * (P % spans) + half;
+    by = (P / spans) % gy;
+    bz = P / (spans * gy);
+    if (bz >= batch) return;  // the flat grid's tail
+  } else {
+    bx = blockIdx.x;
+    by = blockIdx.y;
+    bz = blockIdx.z;
+  }
   const int64_t nblk = seg ? ldq / 32 : rows / 32;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 4;
+  const int64_t b0 = by * 4;
   if (seg) {
     // segment offsets and the prefix sum of their 32-row block counts: given
     // (blk), or an inclusive scan over one thread per segment
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     b_nv[tid] = static_cast<int>(nv);
   }
   __syncthreads();
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kColW;
+  const int64_t c0 = bx * kColW;
   const T* base = src + bz * rows * cols;
   for (int v = tid; v < 128 * VPR; v += blockDim.x) {
     const int tr = v / VPR, cv = v - tr * VPR;
@@ -239,6 +257,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
     if (c0 + oc < cols && b0 + j < nblk) sb[(c0 + oc) * (ldq / 32) + b0 + j] = osc[oc][j];
   }
   if constexpr (BOTH) {
+    const int64_t batch_rows = batch * rows;
     // row layout: in each half of the tile, four lanes per tile row (16
     // columns each, two lanes per 32-element block), so that a store
     // instruction writes 16 whole 64-byte row segments
@@ -272,7 +291,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
       if (r < rows && c0 + qt * 16 < cols) {
         *reinterpret_cast<uint4*>(qr + (bz * rows + r) * cols + c0 + qt * 16) = make_uint4(w[0], w[1], w[2], w[3]);
         if (qt == 0)
-          *reinterpret_cast<uint16_t*>(scr + scale_index(GROUPED, bz * rows + r, c0 / 32, gridDim.z * rows, cols / 32)) =
+          *reinterpret_cast<uint16_t*>(scr + scale_index(GROUPED, bz * rows + r, c0 / 32, batch_rows, cols / 32)) =
               static_cast<uint16_t>(pair);
       }
     }
@@ -316,17 +335,17 @@ void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows,
   if (src_dtype == MOE_F32) {
     if (grouped)
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false, true>), grid, dim3(256), 0, s,
-                 static_cast<const float*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const float*>(src), batch, rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
     else
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<float, false, false>), grid, dim3(256), 0, s,
-                 static_cast<const float*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const float*>(src), batch, rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
   } else {
     if (grouped)
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false, true>), grid, dim3(256), 0, s,
-                 static_cast<const uint16_t*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const uint16_t*>(src), batch, rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
     else
       MOE_LAUNCH("mx_quantize_cols", (mx_cols_kernel<uint16_t, false, false>), grid, dim3(256), 0, s,
-                 static_cast<const uint16_t*>(src), rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
+                 static_cast<const uint16_t*>(src), batch, rows, cols, seg, blk, nseg, ldq, q, sc, nullptr, nullptr);
   }
 }
 
@@ -334,14 +353,15 @@ void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows,
                     uint8_t* sc, uint8_t* qr, uint8_t* scr, hipStream_t s) {
   const int64_t nblk = rows / 32;
   if (nblk == 0 || cols == 0 || batch == 0) return;
-  const dim3 grid(static_cast<unsigned>(cdiv(cols, kColW)), static_cast<unsigned>(cdiv(nblk, 4)),
-                  static_cast<unsigned>(batch));
+  // flat grid of tiles (see mx_cols_kernel), rounded up to whole runs of 16 ids
+  const int64_t tiles = cdiv(cols, kColW) * cdiv(nblk, 4) * batch;
+  const dim3 grid(static_cast<unsigned>(cdiv(tiles, 16) * 16));
   if (src_dtype == MOE_F32)
     MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<float, true, true>), grid, dim3(256), 0, s,
-               static_cast<const float*>(src), rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
+               static_cast<const float*>(src), batch, rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
   else
     MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<uint16_t, true, true>), grid, dim3(256), 0, s,
-               static_cast<const uint16_t*>(src), rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
+               static_cast<const uint16_t*>(src), batch, rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
 }
 
 }  // namespace moe
