@@ -13,15 +13,16 @@ namespace moe {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Round to nearest, ties to even (finite inputs; NaN handling unspecified).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Round to nearest, ties to even: the hardware conversion (v_cvt_pk_bf16_f32,
+// two values per instruction on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
 }
 
 // Element type traits for the two storage types of the data-movement kernels.
