@@ -60,6 +60,27 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
   if (tid == 0) tiles[max_tiles] = make_int4(static_cast<int>(used), 0, 0, 0);
 }
 
+// One workgroup: each expert's cost, then its rank (the number of experts
+// ahead of it: costlier, or as costly with a lower index) is its slot.
+__global__ __launch_bounds__(256) void wgrad_sched_kernel(const int32_t* __restrict__ offsets, int E,
+                                                          int32_t* __restrict__ sched) {
+  __shared__ int32_t cost[kMaxE];
+  static_assert(kMaxE == 256, "one thread per expert");
+  const int t = threadIdx.x;
+  if (t < E) {
+    int32_t n = offsets[t + 1] - offsets[t];
+    if (n < 0) n = 0;
+    cost[t] = (n + 63) / 64 + 3;
+  }
+  __syncthreads();
+  if (t < E) {
+    const int32_t c = cost[t];
+    int rank = 0;
+    for (int e = 0; e < E; ++e) rank += (cost[e] > c || (cost[e] == c && e < t)) ? 1 : 0;
+    sched[rank] = t;
+  }
+}
+
 struct FfnShape {
   int64_t R;
   int E, d, f, prec;
@@ -82,26 +103,15 @@ int tile_bm(int prec, int64_t R, int E) {
 
 size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }
 
-// Workspace layout: [tile table][128-row tile table (MXFP8 backward on 256-row tiles)][dHg][dHu] (backward
-// only)[MX scratch] (MXFP8 only).  The MX SwiGLU-backward GEMM runs on 128 x 128 tiles even where the others
-// use 256 x 256 ones (measured faster: its LDS-staged epilogue on the big tiles takes two half passes).
-size_t one_table_bytes(int64_t R, int E, int bm) {
-  return align_up(static_cast<size_t>(max_m_tiles(R, E, bm) + 1) * sizeof(int4), 256);
-}
-
-bool mx_g3_table(const FfnShape& s, int is_bwd) {
-  return is_bwd && s.prec == MOE_MXFP8 && tile_bm(s.prec, s.R, s.E) != 128;
-}
-
-size_t tiles_bytes(const FfnShape& s, int is_bwd) {
-  size_t b = one_table_bytes(s.R, s.E, tile_bm(s.prec, s.R, s.E));
-  if (mx_g3_table(s, is_bwd)) b += one_table_bytes(s.R, s.E, 128);
-  return b;
+// Workspace layout: [tile table][experts sorted by weight-gradient cost][dHg][dHu] (backward only)[MX scratch]
+// (MXFP8 only).
+size_t tiles_bytes(const FfnShape& s) {
+  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec, s.R, s.E)) + 1) * sizeof(int4), 256);
 }
 
 size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {
-  size_t b = tiles_bytes(s, is_bwd);
-  if (is_bwd) b += 2 * align_up(static_cast<size_t>(s.R) * s.f * elem_bytes(s.prec), 256);
+  size_t b = tiles_bytes(s);
+  if (is_bwd) b += wgrad_sched_bytes() + 2 * align_up(static_cast<size_t>(s.R) * s.f * elem_bytes(s.prec), 256);
   if (s.prec == MOE_MXFP8) b += mx_ffn_scratch_bytes(s.R, s.E, s.d, s.f, is_bwd);
   return b;
 }
@@ -128,6 +138,10 @@ unsigned persistent_grid(int occ, int64_t work) {
   if (g < kNumXcd) g = kNumXcd;
   const int64_t w = static_cast<int64_t>(xcd_grid(work < 1 ? 1 : work));
   return static_cast<unsigned>(g < w ? g : w);
+}
+
+void launch_wgrad_sched(const int32_t* offsets, int E, int32_t* sched, hipStream_t s) {
+  MOE_LAUNCH("wgrad_sched", wgrad_sched_kernel, dim3(1), dim3(256), 0, s, offsets, E, sched);
 }
 
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
@@ -204,7 +218,7 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.x = x_perm; a.wg = w_gate; a.wu = w_up; a.wd = w_down;
   a.o_hg = h_gate; a.o_hu = h_up; a.o_act = a_act; a.act = a_act; a.o_y = y_perm;
   if (prec == MOE_MXFP8) {
-    char* mxs = static_cast<char*>(ws) + tiles_bytes(sh, 0);
+    char* mxs = static_cast<char*>(ws) + tiles_bytes(sh);
     return mx_ffn_fwd(a, mt, static_cast<const char*>(mx_wcache), static_cast<const uint8_t*>(x_mx), mxs, s);
   }
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
@@ -237,7 +251,7 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   char* wsb = static_cast<char*>(ws);
   int4* tiles = reinterpret_cast<int4*>(wsb);
   const size_t hbytes = align_up(static_cast<size_t>(R) * f * elem_bytes(prec), 256);
-  const size_t tb = tiles_bytes(sh, 1);
+  const size_t tb = tiles_bytes(sh) + wgrad_sched_bytes();
   void* dhg = wsb + tb;
   void* dhu = wsb + tb + hbytes;
   launch_tile_map(offsets, E, bm, R, mt, tiles, s);
@@ -251,12 +265,9 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.hg = h_gate; a.hu = h_up; a.act = a_act; a.dy = dy_perm;
   a.o_dhg = dhg; a.o_dhu = dhu; a.dhg = dhg; a.dhu = dhu;
   a.o_dx = dx_perm; a.o_dwg = dw_gate; a.o_dwu = dw_up; a.o_dwd = dw_down;
-  if (mx_g3_table(sh, 1) && R > 0) {
-    a.max_tiles128 = max_m_tiles(R, E, 128);
-    int4* t128 = reinterpret_cast<int4*>(wsb + one_table_bytes(R, E, bm));
-    a.tiles128 = t128;
-    launch_tile_map(offsets, E, 128, R, a.max_tiles128, t128, s);
-  }
+  int32_t* wsched = reinterpret_cast<int32_t*>(wsb + tiles_bytes(sh));
+  launch_wgrad_sched(offsets, E, wsched, s);
+  a.wsched = wsched;
   if (prec == MOE_MXFP8) {
     char* mxs = wsb + tb + 2 * hbytes;
     return mx_ffn_bwd(a, mt, mx_blk_offsets, static_cast<const char*>(mx_wcache), static_cast<const uint8_t*>(dy_mx),

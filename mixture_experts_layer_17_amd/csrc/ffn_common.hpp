@@ -27,8 +27,7 @@ struct FfnArgs {
                            // entry [max_tiles] = {number of live tiles, 0, 0, 0}
   int64_t max_tiles;
   int bm;                  // row-tile height the tile table was built for
-  const int4* tiles128;    // MXFP8 backward with bm = 256: a 128-row table for the SwiGLU-backward GEMM, else null
-  int64_t max_tiles128;
+  const int32_t* wsched;   // backward: the experts sorted by weight-gradient cost (wgrad_tile_sorted)
   int E, d, f;
   int64_t R;
   // inputs
@@ -56,36 +55,43 @@ inline unsigned xcd_grid(int64_t total) {
   return static_cast<unsigned>(cdiv(total, kNumXcd) * kNumXcd);
 }
 
-// Weight-gradient tile order.  Expert e has a gm x gn grid of output tiles;
-// tiles in a block of GM x GN read the same GM operand slices along M and GN
-// along N.  Workgroups are handed to the XCDs round-robin by hardware id, so
-// the S = GM*GN tiles of one block get ids h, h+8, ..., h+8(S-1) (one XCD, one
-// L2), while the 8 blocks of a run of 8*S ids sit on 8 different XCDs (a heavily
-// loaded expert still spreads over the whole chip).  Returns false for ids
-// past the last tile; the grid is E*gm*gn.
-__device__ __forceinline__ bool wgrad_tile(int64_t h, int E, int gm, int gn, int& e, int& mt, int& nt) {
-  const int GM = gm % 2 == 0 ? 2 : 1;
-  const int GN = gn % 4 == 0 ? 4 : gn % 2 == 0 ? 2 : 1;
-  const int S = GM * GN;
-  const int64_t per_e = static_cast<int64_t>(gm / GM) * (gn / GN);
-  const int64_t ng = per_e * E;  // blocks
-  const int64_t run = h / (kNumXcd * S), q = h % (kNumXcd * S);
-  int64_t g;
-  int w;
-  if ((run + 1) * kNumXcd <= ng) {
-    g = run * kNumXcd + q % kNumXcd;
-    w = static_cast<int>(q / kNumXcd);
-  } else {  // last, partial run: blocks in hardware order
-    g = run * kNumXcd + q / S;
-    w = static_cast<int>(q % S);
-    if (g >= ng) return false;
+// Weight-gradient tile order for one workgroup per tile (G4, G6), from the
+// experts sorted by cost (sched[0, E), as launch_wgrad_sched writes it).  The
+// hardware deals workgroup ids round-robin over the 8 XCDs; id h runs on XCD
+// x = h % 8 as that XCD's q-th workgroup (q = h / 8).  The sorted experts go in
+// rounds of 8: in round 0 (the 8 costliest) each expert's tiles spread over all
+// 8 XCDs, so a heavily routed expert still fills the chip; in every later round
+// XCD x takes expert 8r + x whole, so one L2 serves all of that expert's operand
+// slices.  Each XCD holds ntile slots per round, heaviest rounds first, and the
+// grid is 8 * ntile * ceil(E / 8).  False for slots past the last expert.
+__device__ __forceinline__ bool wgrad_tile_sorted(int64_t h, int E, int ntile, const int32_t* sched, int& e,
+                                                  int& local) {
+  const int x = static_cast<int>(h % kNumXcd);
+  const int64_t q = h / kNumXcd;
+  const int r = static_cast<int>(q / ntile);
+  int j;
+  if (r == 0) {
+    const int64_t t = q * kNumXcd + x;  // the round's 8 * ntile tiles, dealt over the XCDs
+    j = static_cast<int>(t / ntile);
+    local = static_cast<int>(t % ntile);
+  } else {
+    j = r * kNumXcd + x;
+    local = static_cast<int>(q - static_cast<int64_t>(r) * ntile);
   }
-  e = static_cast<int>(g / per_e);
-  const int rem = static_cast<int>(g % per_e), bn = gn / GN;
-  mt = (rem / bn) * GM + w / GN;
-  nt = (rem % bn) * GN + w % GN;
+  if (j >= E) return false;
+  e = sched[j];
   return true;
 }
+inline int64_t wgrad_sorted_grid(int E, int ntile) {
+  return static_cast<int64_t>(kNumXcd) * ntile * ((E + kNumXcd - 1) / kNumXcd);
+}
+
+// The experts sorted by weight-gradient cost, largest first (ties: lower
+// index), written by a one-workgroup kernel from the routing offsets so the
+// host never waits: sched[0, E) int32 on the device.  An expert's cost is
+// ceil(n_e / 64) + 3 (its K-steps plus an allowance for the epilogue).
+inline size_t wgrad_sched_bytes() { return align_up(static_cast<size_t>(kMaxE) * 4, 256); }
+void launch_wgrad_sched(const int32_t* offsets, int E, int32_t* sched, hipStream_t s);
 
 // Persistent launches (ffn.hip).  occupancy: resident workgroups per compute
 // unit of `kernel` at `threads` per workgroup (at least 1).  persistent_grid:

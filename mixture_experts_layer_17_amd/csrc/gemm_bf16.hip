@@ -256,7 +256,7 @@ struct Tile {
 };
 
 // Tile of hardware id h (rows-by-expert GEMMs: XCD-contiguous ranges over the
-// `live` table entries times the N tiles; weight gradients: wgrad_tile).
+// `live` table entries times the N tiles; weight gradients: wgrad_tile_sorted).
 // False once h is past the last tile; for a fixed h mod 8 that holds for every
 // larger h too, so a workgroup stepping h by the grid size stops there.
 template <class C, int KIND>
@@ -319,8 +319,9 @@ __device__ __forceinline__ bool make_tile(const FfnArgs& p, int64_t h, int64_t l
     // slices kept on one XCD, an expert's blocks spread over all XCDs
     const int gm = KIND == kG4 ? (f + C::BM - 1) / C::BM : (d + C::BM - 1) / C::BM;
     const int gn = KIND == kG4 ? (d + C::BN - 1) / C::BN : 2 * ((f + C::BN - 1) / C::BN);
-    int e, mt, ntile;
-    if (!wgrad_tile(h, p.E, gm, gn, e, mt, ntile)) return false;
+    int e, local;
+    if (!wgrad_tile_sorted(h, p.E, gm * gn, p.wsched, e, local)) return false;
+    const int mt = local / gn, ntile = local % gn;
     e = __builtin_amdgcn_readfirstlane(e);
     const int64_t seg0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
     const int K = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]) - static_cast<int>(seg0);
@@ -347,115 +348,6 @@ __device__ __forceinline__ bool make_tile(const FfnArgs& p, int64_t h, int64_t l
     }
   }
   return true;
-}
-
-// SwiGLU-backward epilogue of the 256 x 256 tiles (G3) with Hg, Hu staged
-// through LDS.  Each wave owns 16 KB of the (then idle) LDS rings: two buffers
-// of one 32-row block of its 128 x 64 sub-tile, Hg then Hu (4 KB each), filled
-// with coalesced LDS-DMA loads (eight whole 128-byte rows per instruction).
-// Within a buffer, 128-byte row r keeps global 16-byte chunk q at physical
-// chunk q ^ ((r >> 1) & 7), so that reading 32 rows at one chunk (the
-// accumulator layout) is free of bank conflicts.
-template <class C>
-__device__ __forceinline__ void g3_stage(const FfnArgs& p, const Tile& t, int i, uint16_t* buf, int wm, int wn,
-                                         int lane) {
-  static_assert(C::WTN == 64, "one 128-byte row per wave and block");
-  const int64_t f = p.f;
-  const int64_t colbase = t.n0 + wn * C::WTN;
-  const int64_t bytes = (static_cast<int64_t>(t.rows) * f - colbase) * 2;
-  const int64_t o = t.row0 * f + colbase;
-  const __amdgpu_buffer_rsrc_t rg = rsrc(static_cast<const uint16_t*>(p.hg) + o, bytes);
-  const __amdgpu_buffer_rsrc_t ru = rsrc(static_cast<const uint16_t*>(p.hu) + o, bytes);
-  const int rbase = wm * C::WTM + i * 32;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = u * 8 + (lane >> 3);
-    const int q = (lane & 7) ^ ((r >> 1) & 7);
-    const int voff = static_cast<int>(((rbase + r) * f + q * 8) * 2);
-    dma16(rg, buf + u * 512, voff);
-    dma16(ru, buf + 2048 + u * 512, voff);
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void g3_block(const Acc<C>& acc, const FfnArgs& p, const Tile& t, int i,
-                                         const uint16_t* buf, int wm, int wn, int lane) {
-  const int rl = lane & 31, h = lane >> 5;
-  const int64_t f = p.f;
-  uint16_t* dg = static_cast<uint16_t*>(p.o_dhg) + t.row0 * f + t.n0;
-  uint16_t* du = static_cast<uint16_t*>(p.o_dhu) + t.row0 * f + t.n0;
-  const int row = wm * C::WTM + i * 32 + rl;
-#pragma unroll
-  for (int j = 0; j < C::TN; ++j) {
-    float da[2][8];
-    to_chunks(acc[i][j], da);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = 4 * j + 2 * c + h;  // 16-byte chunk of the wave's 64 columns
-      const int ph = q ^ ((rl >> 1) & 7);
-      const uint4 vg = *reinterpret_cast<const uint4*>(buf + rl * 64 + ph * 8);
-      const uint4 vu = *reinterpret_cast<const uint4*>(buf + 2048 + rl * 64 + ph * 8);
-      const int col = wn * C::WTN + q * 8;
-      if (row < t.rows && col < t.cols) {
-        float g[8], u[8], og[8], ou[8];
-        Elem<uint16_t>::unpack(vg, g);
-        Elem<uint16_t>::unpack(vu, u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float sg = sigmoid_f(g[e]);
-          ou[e] = da[c][e] * g[e] * sg;
-          og[e] = da[c][e] * u[e] * sg * (1.0f + g[e] * (1.0f - sg));
-        }
-        const int64_t o = row * f + col;
-        store16<false>(dg + o, pack8(og));
-        store16<false>(du + o, pack8(ou));
-      }
-    }
-  }
-}
-
-// Plain output of the 256 x 256 tiles through LDS, as whole lines.  Each wave
-// writes two 32-row blocks of its 128 x 64 sub-tile as bf16 into its 8 KB of
-// the idle ring slot (row r keeps 16-byte chunk q at q ^ ((r >> 1) & 7):
-// conflict-free both ways), reads them back eight whole 128-byte rows per
-// instruction and stores those; twice.  Only this wave touches its buffer.
-// NT: the non-temporal hint, for outputs no kernel reads soon (the weight
-// gradients); G5's dX rows, read by the dispatch backward right after, keep
-// ordinary stores.
-template <class C, bool NT = true>
-__device__ __forceinline__ void epi_staged_store(const Acc<C>& acc, uint16_t* buf, uint16_t* dst, int64_t ld,
-                                                 int rows_valid, int cols_valid, int lane, int wm, int wn) {
-  static_assert(C::WTN == 64 && C::TM % 2 == 0, "two 32 x 64 blocks per pass");
-  const int rl = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int pass = 0; pass < C::TM / 2; ++pass) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        float v[2][8];
-        to_chunks(acc[2 * pass + b][j], v);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int q = 4 * j + 2 * c + h;
-          *reinterpret_cast<uint4*>(buf + b * 2048 + rl * 64 + (q ^ ((rl >> 1) & 7)) * 8) = pack8(v[c]);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = u * 8 + (lane >> 3), p = lane & 7;
-        const int q = p ^ ((r >> 1) & 7);
-        const uint4 v = *reinterpret_cast<const uint4*>(buf + b * 2048 + r * 64 + p * 8);
-        const int row = wm * C::WTM + (2 * pass + b) * 32 + r, col = wn * C::WTN + q * 8;
-        if (row < rows_valid && col < cols_valid) {
-          if (NT) store16_nt(dst + row * ld + col, v);
-          else *reinterpret_cast<uint4*>(dst + row * ld + col) = v;
-        }
-      }
-  }
 }
 
 // Persistent grid (workgroups loop over tiles) or one workgroup per tile; see
@@ -624,7 +516,7 @@ void ffn_bf16_kernel(FfnArgs p) {
         if (kt == 0 && 1 < nk && pre < 2) issue_b(cur, 1, g + 1);
         if (kt + 2 < nk) issue_b(cur, kt + 2, g + kt + 2);
       }
-      if (kStaged && kt + 1 == nk) g3_stage<C>(p, cur, 0, stage_buf((g + nk) % 2), wm, wn, lane);
+      if (kStaged && kt + 1 == nk) g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 0, stage_buf((g + nk) % 2), wm, wn, lane);
       if (C::kRegEpi && !kStaged && kt + 1 == nk && more) {
         const int nk2 = (nxt.K + C::BK - 1) / C::BK;
         for (int s = 0; s < kPre && s < nk2; ++s) {
@@ -660,15 +552,15 @@ void ffn_bf16_kernel(FfnArgs p) {
         uint16_t* b0 = stage_buf(g % 2);
         uint16_t* b1 = stage_buf((g + 1) % 2);
         __syncthreads();  // the last step's slot is free
-        g3_stage<C>(p, cur, 1, b1, wm, wn, lane);
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 1, b1, wm, wn, lane);
         wait_vm<0>();
-        g3_block<C>(acc, p, cur, 0, b0, wm, wn, lane);
-        g3_block<C>(acc, p, cur, 1, b1, wm, wn, lane);
-        g3_stage<C>(p, cur, 2, b0, wm, wn, lane);
-        g3_stage<C>(p, cur, 3, b1, wm, wn, lane);
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 0, b0, wm, wn, lane);
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 1, b1, wm, wn, lane);
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 2, b0, wm, wn, lane);
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 3, b1, wm, wn, lane);
         wait_vm<0>();
-        g3_block<C>(acc, p, cur, 2, b0, wm, wn, lane);
-        g3_block<C>(acc, p, cur, 3, b1, wm, wn, lane);
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 2, b0, wm, wn, lane);
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 3, b1, wm, wn, lane);
         __syncthreads();  // the LDS is the ring again
       }
     } else if constexpr (!C::kRegEpi) {
@@ -716,8 +608,10 @@ int launch_cfg(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s) {
     case kG2: launch_kind<C, kG2>("G2_bf16", a, nd * max_tiles, s); break;
     case kG3: launch_kind<C, kG3>("G3_bf16", a, nf * max_tiles, s); break;
     case kG5: launch_kind<C, kG5>("G5_bf16", a, nd * max_tiles, s); break;
-    case kG4: launch_kind<C, kG4>("G4_bf16", a, a.E * cdiv(a.f, C::BM) * nd, s); break;
-    case kG6: launch_kind<C, kG6>("G6_bf16", a, a.E * cdiv(a.d, C::BM) * 2 * nf, s); break;
+    case kG4: launch_kind<C, kG4>("G4_bf16", a, wgrad_sorted_grid(a.E, static_cast<int>(cdiv(a.f, C::BM) * nd)), s); break;
+    case kG6:
+      launch_kind<C, kG6>("G6_bf16", a, wgrad_sorted_grid(a.E, static_cast<int>(cdiv(a.d, C::BM) * 2 * nf)), s);
+      break;
     default: return MOE_EINVAL;
   }
   return launch_status();

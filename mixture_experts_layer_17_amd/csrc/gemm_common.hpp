@@ -14,6 +14,20 @@ namespace moe {
 namespace gemm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// 16-byte LDS accesses go through an ext_vector type rather than a struct such
+// as uint4: only then does the compiler's alias information tell an LDS read
+// or write apart from the LDS-DMA loads still in flight into another ring slot,
+// instead of waiting for all of them before it (a full vmcnt wait).
+typedef int lds16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_get16(const void* p) {
+  const lds16_t v = *reinterpret_cast<const lds16_t*>(p);
+  return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                    static_cast<uint32_t>(v[3]));
+}
+__device__ __forceinline__ void lds_put16(void* p, const uint4& u) {
+  const lds16_t v = {static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w)};
+  *reinterpret_cast<lds16_t*>(p) = v;
+}
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -347,6 +361,121 @@ __device__ __forceinline__ void epi_regs_swiglu_bwd(const Acc<C>& acc, const Ffn
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-private epilogues of the 256 x 256 tiles (8 waves of 128 x 64, tiles
+// computed transposed) through LDS the main loop no longer uses: each wave
+// owns 8 KB of a ring slot (stage buffer `buf`, bf16 elements).
+// ---------------------------------------------------------------------------
+
+// SwiGLU-backward epilogue of the 256 x 256 tiles (G3) with Hg, Hu staged
+// through LDS.  Each wave owns 16 KB of the (then idle) LDS rings: two buffers
+// of one 32-row block of its 128 x 64 sub-tile, Hg then Hu (4 KB each), filled
+// with coalesced LDS-DMA loads (eight whole 128-byte rows per instruction).
+// Within a buffer, 128-byte row r keeps global 16-byte chunk q at physical
+// chunk q ^ ((r >> 1) & 7), so that reading 32 rows at one chunk (the
+// accumulator layout) is free of bank conflicts.
+template <class C>
+__device__ __forceinline__ void g3_stage(const FfnArgs& p, int64_t row0, int rows, int n0, int i, uint16_t* buf,
+                                         int wm, int wn, int lane) {
+  static_assert(C::WTN == 64, "one 128-byte row per wave and block");
+  const int64_t f = p.f;
+  const int64_t colbase = n0 + wn * C::WTN;
+  const int64_t bytes = (static_cast<int64_t>(rows) * f - colbase) * 2;
+  const int64_t o = row0 * f + colbase;
+  const __amdgpu_buffer_rsrc_t rg = rsrc(static_cast<const uint16_t*>(p.hg) + o, bytes);
+  const __amdgpu_buffer_rsrc_t ru = rsrc(static_cast<const uint16_t*>(p.hu) + o, bytes);
+  const int rbase = wm * C::WTM + i * 32;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = u * 8 + (lane >> 3);
+    const int q = (lane & 7) ^ ((r >> 1) & 7);
+    const int voff = static_cast<int>(((rbase + r) * f + q * 8) * 2);
+    dma16(rg, buf + u * 512, voff);
+    dma16(ru, buf + 2048 + u * 512, voff);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void g3_block(const Acc<C>& acc, const FfnArgs& p, int64_t row0, int rows, int n0,
+                                         int cols, int i, const uint16_t* buf, int wm, int wn, int lane) {
+  const int rl = lane & 31, h = lane >> 5;
+  const int64_t f = p.f;
+  uint16_t* dg = static_cast<uint16_t*>(p.o_dhg) + row0 * f + n0;
+  uint16_t* du = static_cast<uint16_t*>(p.o_dhu) + row0 * f + n0;
+  const int row = wm * C::WTM + i * 32 + rl;
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    float da[2][8];
+    to_chunks(acc[i][j], da);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int q = 4 * j + 2 * c + h;  // 16-byte chunk of the wave's 64 columns
+      const int ph = q ^ ((rl >> 1) & 7);
+      const uint4 vg = lds_get16(buf + rl * 64 + ph * 8);
+      const uint4 vu = lds_get16(buf + 2048 + rl * 64 + ph * 8);
+      const int col = wn * C::WTN + q * 8;
+      if (row < rows && col < cols) {
+        float g[8], u[8], og[8], ou[8];
+        Elem<uint16_t>::unpack(vg, g);
+        Elem<uint16_t>::unpack(vu, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = sigmoid_f(g[e]);
+          ou[e] = da[c][e] * g[e] * sg;
+          og[e] = da[c][e] * u[e] * sg * (1.0f + g[e] * (1.0f - sg));
+        }
+        const int64_t o = row * f + col;
+        store16<false>(dg + o, pack8(og));
+        store16<false>(du + o, pack8(ou));
+      }
+    }
+  }
+}
+
+// Plain output of the 256 x 256 tiles through LDS, as whole lines.  Each wave
+// writes two 32-row blocks of its 128 x 64 sub-tile as bf16 into its 8 KB of
+// the idle ring slot (row r keeps 16-byte chunk q at q ^ ((r >> 1) & 7):
+// conflict-free both ways), reads them back eight whole 128-byte rows per
+// instruction and stores those; twice.  Only this wave touches its buffer.
+// NT: the non-temporal hint, for outputs no kernel reads soon (the weight
+// gradients); G5's dX rows, read by the dispatch backward right after, keep
+// ordinary stores.
+template <class C, bool NT = true>
+__device__ __forceinline__ void epi_staged_store(const Acc<C>& acc, uint16_t* buf, uint16_t* dst, int64_t ld,
+                                                 int rows_valid, int cols_valid, int lane, int wm, int wn) {
+  static_assert(C::WTN == 64 && C::TM % 2 == 0, "two 32 x 64 blocks per pass");
+  const int rl = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int pass = 0; pass < C::TM / 2; ++pass) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        float v[2][8];
+        to_chunks(acc[2 * pass + b][j], v);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int q = 4 * j + 2 * c + h;
+          lds_put16(buf + b * 2048 + rl * 64 + (q ^ ((rl >> 1) & 7)) * 8, pack8(v[c]));
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = u * 8 + (lane >> 3), p = lane & 7;
+        const int q = p ^ ((r >> 1) & 7);
+        const uint4 v = lds_get16(buf + b * 2048 + r * 64 + p * 8);
+        const int row = wm * C::WTM + (2 * pass + b) * 32 + r, col = wn * C::WTN + q * 8;
+        if (row < rows_valid && col < cols_valid) {
+          if (NT) store16_nt(dst + row * ld + col, v);
+          else *reinterpret_cast<uint4*>(dst + row * ld + col) = v;
+        }
+      }
   }
 }
 

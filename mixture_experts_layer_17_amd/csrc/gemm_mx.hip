@@ -33,26 +33,41 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kNoSplit = 0x7FFFFFFF;
 
-// Tile configuration: BM x BN outputs, WM x WN waves; K-step BK = 128 fp8
-// elements (two MFMA K-slices); two LDS stages per operand.
-template <int BM_, int BN_, int WM_, int WN_>
+// Tile configuration: BM x BN outputs, WM x WN waves, K-step BK fp8 elements
+// (128: two MFMA K-slices; 64: one), NS LDS stages per operand.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct MxCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int BK = 128;
   static constexpr int kA = BM * BK, kB = BN * BK;  // bytes per stage
-  // scale words: per stage, two groups (the K-step's four blocks may straddle two) x [A: 1 KB, B: 2 x 1 KB]
+  // scale words: per stage, two groups (the K-step's blocks may straddle two) x [A: 1 KB, B: 2 x 1 KB]
   static constexpr int kScaleStage = 2 * 3 * 1024;
-  static constexpr int kScales = 2 * kScaleStage;
+  static constexpr int kScales = NS * kScaleStage;
   static_assert(BM <= 256 && BN <= 256, "one 1 KB scale run per operand (half) and group");
+  static_assert(BK == 64 || BK == 128, "one or two MFMA K-slices per step");
   static constexpr int kEpi = cmax(2 * BM * (BN / 2 + 8), BM * (BN + 8));  // bf16 elements
-  static constexpr int kLds = cmax((2 * kA + 2 * kB + kScales) / 2, kEpi);  // bf16 elements
+  static constexpr int kLds = cmax((NS * kA + NS * kB + kScales) / 2, kEpi);  // bf16 elements
   static_assert(kLds * 2 <= 160 * 1024, "LDS budget");
+  // LDS-DMA data loads (1 KB each) per wave per step (the scale runs come on top, one per wave at most)
+  static constexpr int kDmaPerStep = (kA + kB) / 1024 / kWaves;
 };
-using MxBig = MxCfg<256, 256, 2, 4>;
-using MxSmall = MxCfg<128, 128, 2, 2>;
+// K-step 128 on two stages.  (K-step 64 on four stages, three steps of loads
+// in flight, measured 20-25% slower on every MX GEMM: each step starts with all
+// waves past one barrier asking for their fragments at once, and shorter steps
+// expose that LDS latency twice as often.)
+using MxBig = MxCfg<256, 256, 2, 4, 128, 2>;
+using MxBigP = MxBig;
+using MxSmall = MxCfg<128, 128, 2, 2, 128, 2>;
+
+// 16-byte chunk swizzle of a K-contiguous fp8 tile row (BK bytes): a fragment
+// read has 16 lanes on 16 consecutive rows at one chunk; the swizzle spreads
+// them over all 64 banks.
+template <int BK>
+__device__ __forceinline__ int mx_swz(int row) {
+  return BK == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
 
 // K-contiguous fp8 operand with block scales: element (mn, k) at
 // q[mn*ld + k_base + k]; k >= ksplit reads the second matrix at k - ksplit.
@@ -75,18 +90,21 @@ struct MxKc {
   int64_t gs;      // bytes between scale groups
 };
 
-// LDS-DMA loads of a ROWS x 128-byte tile (K-step at k0).
+// LDS-DMA loads of a ROWS x BK-byte tile (K-step at k0).
 template <class C, int ROWS, bool DUAL>
 __device__ __forceinline__ void mx_dma(const MxKc& op, int k0, uint8_t* dst, int wave, int lane) {
-  constexpr int NI = ROWS / 8;  // 8 rows of 128 bytes per 1 KB instruction
+  constexpr int CPR = C::BK / 16;  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;    // rows per 1 KB instruction
+  constexpr int NI = ROWS / RPI;
   static_assert(NI % C::kWaves == 0, "tile does not split over the waves");
   const bool hi = !DUAL && k0 >= op.ksplit;
   const int64_t kk = op.k_base + (hi ? k0 - op.ksplit : k0);
-  const int rl = lane >> 3, ph = lane & 7;
+  const int rl = lane / CPR, ph = lane % CPR;
 #pragma unroll
   for (int u = 0; u < NI / C::kWaves; ++u) {
     const int i = wave + u * C::kWaves;
-    int row = i * 8 + rl;
+    const int trow = i * RPI + rl;
+    int row = trow;
     const uint8_t* q = hi ? op.q1 : op.q0;
     if constexpr (DUAL) {
       if (i >= NI / 2) q = op.q1;
@@ -95,7 +113,7 @@ __device__ __forceinline__ void mx_dma(const MxKc& op, int k0, uint8_t* dst, int
     const int rows = op.mn_valid < (DUAL ? ROWS / 2 : ROWS) ? op.mn_valid : (DUAL ? ROWS / 2 : ROWS);
     // [q + kk, q + rows*ld): ends with the last valid row
     const __amdgpu_buffer_rsrc_t r = rsrc(q + kk, static_cast<int64_t>(rows) * op.ld - kk);
-    const int lc = ph ^ ((i * 8 + rl) >> 1 & 7);
+    const int lc = ph ^ mx_swz<C::BK>(trow);
     dma16(r, dst + i * 1024, static_cast<int>(row * op.ld + lc * 16));
   }
 }
@@ -108,14 +126,19 @@ __device__ __forceinline__ void scale_dma(const uint8_t* s, int64_t gs, int64_t 
   dma16(r, dst, lane * 16);
 }
 
-// One fp8 MFMA operand (32 bytes) from a 128-byte-row tile: row `row`, K-slice ks.
+// One fp8 MFMA operand (32 bytes) from a BK-byte-row tile: row `row`, K-slice ks.
+// (Read as an ext_vector type, not a struct: the compiler then knows the read
+// cannot be the target of an LDS-DMA load still in flight into the other stage
+// and does not wait for all of them first, which serialised each step's loads
+// with its MFMAs.)
+template <int BK>
 __device__ __forceinline__ i32x8 mx_frag(const uint8_t* t, int row, int ks, int g) {
-  const int sw = (row >> 1) & 7;
-  const uint4 lo = *reinterpret_cast<const uint4*>(t + row * 128 + (((ks * 4 + g) ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(t + row * 128 + (((ks * 4 + 2 + g) ^ sw) << 4));
+  const int sw = mx_swz<BK>(row);
+  const lds16_t lo = *reinterpret_cast<const lds16_t*>(t + row * BK + (((ks * 4 + g) ^ sw) << 4));
+  const lds16_t hi = *reinterpret_cast<const lds16_t*>(t + row * BK + (((ks * 4 + 2 + g) ^ sw) << 4));
   i32x8 v;
-  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
   return v;
 }
 
@@ -130,13 +153,32 @@ __device__ __forceinline__ int b_row(int wn, int j) {
   }
 }
 
-// C = A B^T over K = [0, K), both operands K-contiguous fp8 with block scales.
-// Each K-step's scale words (groups G and, when the step starts mid-group,
-// G+1) come in by LDS-DMA with the data; a lane shifts its row's four bytes
-// out of the two words.
-template <class C, bool BDUAL>
+// Wait until at most `steps` K-steps of data loads (N per step) are outstanding.
+template <int N, int MAXS>
+__device__ __forceinline__ void mx_wait_steps(int steps) {
+  static_assert(N * MAXS < 16, "vmcnt immediate");
+  if constexpr (MAXS >= 2) {
+    if (steps >= 2) { wait_vm<2 * N>(); return; }
+  }
+  if constexpr (MAXS >= 1) {
+    if (steps >= 1) { wait_vm<N>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// C = A B^T over K = [0, K), both operands K-contiguous fp8 with block scales,
+// through NS LDS stages: steps 0 .. NS-2 are issued up front and, right after
+// the barrier of step kt, step kt + NS - 1 (into the stage step kt - 1 used).
+// Each step's scale words (the 4-block group holding its first block and,
+// when its blocks run past that group, the next) come in by LDS-DMA with the
+// data; a lane shifts its row's bytes out of the two words.  The wait before
+// step kt leaves outstanding only as many loads as the data loads of the steps
+// issued after it (loads complete in issue order; a scale run issued on top
+// only makes the wait stricter).
+template <class C, bool BDUAL, bool TR = false>
 __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, int K, uint8_t* lds, int tid,
                                             Acc<C>& acc) {
+  constexpr int NS = C::NS, BK = C::BK, NSL = BK / 64;
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -146,83 +188,95 @@ __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, in
     for (int j = 0; j < C::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nk = (K + C::BK - 1) / C::BK;
+  const int nk = (K + BK - 1) / BK;
   if (nk == 0) return;
-  uint8_t* qa = lds;                                          // A stages
-  uint8_t* qb = lds + 2 * C::kA;                              // B stages
-  uint8_t* sl = lds + 2 * C::kA + 2 * C::kB;                  // [2 stages][2 groups][A 1 KB | B 2 KB]
-  // the problem's K offset in blocks decides how K-steps sit in the groups (the same for A and B)
-  const int o = static_cast<int>((aop.k_base / 32) & 3);
+  uint8_t* qa = lds;                            // A stages
+  uint8_t* qb = lds + NS * C::kA;               // B stages
+  uint8_t* sl = lds + NS * (C::kA + C::kB);     // [NS stages][2 groups][A 1 KB | B 2 KB]
   const int arows = aop.mn_valid < C::BM ? aop.mn_valid : C::BM;
   constexpr int BH = BDUAL ? C::BN / 2 : C::BN;
   const int brows = bop.mn_valid < BH ? bop.mn_valid : BH;
-  auto issue = [&](int kt) {
-    const int k0 = kt * C::BK;
-    mx_dma<C, C::BM, false>(aop, k0, qa + (kt & 1) * C::kA, wave, lane);
-    mx_dma<C, C::BN, BDUAL>(bop, k0, qb + (kt & 1) * C::kB, wave, lane);
-    // scale runs: slot = group (0, 1) x {A, B half 0, B half 1}
+  // first block of step kt inside its matrix (K-steps of a split operand restart at the split)
+  auto first_block = [&](int kt) -> int64_t {
+    const int k0 = kt * BK;
     const bool hi = !BDUAL && k0 >= aop.ksplit;
-    const int kk = hi ? k0 - aop.ksplit : k0;
-    const int64_t G = (aop.k_base / 32 + kk / 32) >> 2;
-    uint8_t* st = sl + (kt & 1) * C::kScaleStage;
+    return aop.k_base / 32 + (hi ? k0 - aop.ksplit : k0) / 32;
+  };
+  auto issue = [&](int kt) {
+    const int k0 = kt * BK;
+    const int st = kt % NS;
+    mx_dma<C, C::BM, false>(aop, k0, qa + st * C::kA, wave, lane);
+    mx_dma<C, C::BN, BDUAL>(bop, k0, qb + st * C::kB, wave, lane);
+    // scale runs, dealt round-robin over the waves: run = group (0, 1) x {A, B half 0, B half 1}
+    const bool hi = !BDUAL && k0 >= aop.ksplit;
+    const int64_t b0 = first_block(kt);
+    const int64_t G = b0 >> 2;
+    const bool two = (b0 & 3) + BK / 32 > 4;  // the step's blocks run into the next group
 #pragma unroll
-    for (int slot = 0; slot < 6; ++slot) {
-      const int grp = slot / 3, part = slot % 3;
-      if (grp == 1 && o == 0) continue;
-      if (part == 2 && !BDUAL) continue;
-      if (wave != slot % C::kWaves) continue;
-      uint8_t* dst = st + grp * 3072 + part * 1024;
+    for (int run = 0; run < 6; ++run) {
+      const int grp = run / 3, part = run % 3;
+      if (run % C::kWaves != wave || (grp == 1 && !two) || (part == 2 && !BDUAL)) continue;
+      uint8_t* dst = sl + st * C::kScaleStage + grp * 3072 + part * 1024;
       if (part == 0)
         scale_dma(hi ? aop.s1 : aop.s0, aop.gs, G + grp, arows, dst, lane);
       else
         scale_dma((part == 2 || (!BDUAL && hi)) ? bop.s1 : bop.s0, bop.gs, G + grp, brows, dst, lane);
     }
   };
-  // bytes of this step's 4 blocks that lie inside the problem's K range
-  auto kmask = [&](int kt) -> uint32_t {
-    const int nb = (aop.k_valid - kt * C::BK) / 32;
-    return nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
-  };
-  // a row's four scale bytes from the staged words
-  auto word = [&](const uint8_t* st, int part, int row) -> uint32_t {
-    const uint32_t w0 = reinterpret_cast<const uint32_t*>(st + part * 1024)[row];
-    if (o == 0) return w0;
-    const uint32_t w1 = reinterpret_cast<const uint32_t*>(st + 3072 + part * 1024)[row];
-    return (w0 >> (8 * o)) | (w1 << (32 - 8 * o));
-  };
-  issue(0);
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < nk) issue(s0);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<0>();
+    const int ahead = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+    mx_wait_steps<C::kDmaPerStep, NS - 2>(ahead);
     __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1);
-    const uint8_t* as = qa + (kt & 1) * C::kA;
-    const uint8_t* bs = qb + (kt & 1) * C::kB;
-    const uint8_t* ss = sl + (kt & 1) * C::kScaleStage;
-    const uint32_t m = kmask(kt);
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    const int st = kt % NS;
+    const uint8_t* as = qa + st * C::kA;
+    const uint8_t* bs = qb + st * C::kB;
+    const uint8_t* ss = sl + st * C::kScaleStage;
+    // the step's blocks from byte o of the staged group word on; those past the problem's K range get
+    // zero-weight scales
+    const int o = static_cast<int>(first_block(kt) & 3);
+    const int nb = (aop.k_valid - kt * BK) / 32;
+    const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
+    auto word = [&](int part, int row) -> uint32_t {
+      const uint32_t w0 = reinterpret_cast<const uint32_t*>(ss + part * 1024)[row];
+      if (o == 0) return w0;
+      const uint32_t w1 = reinterpret_cast<const uint32_t*>(ss + 3072 + part * 1024)[row];
+      return (w0 >> (8 * o)) | (w1 << (32 - 8 * o));
+    };
+    // lane (g, m) needs block 2 ks + g of its row for K-slice ks: the word shifted down by g bytes puts it at
+    // byte 2 ks, which the MFMA's scale operand selects (op_sel)
     uint32_t ca[C::TM], cb[C::TN];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) ca[i] = word(ss, 0, wm * C::WTM + i * 32 + (lane & 31)) & m;
+    for (int i = 0; i < C::TM; ++i) ca[i] = (word(0, wm * C::WTM + i * 32 + (lane & 31)) & m) >> (8 * g);
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       const int r = b_row<C, BDUAL>(wn, j) + (lane & 31);
-      cb[j] = (BDUAL && r >= C::BN / 2 ? word(ss, 2, r - C::BN / 2) : word(ss, 1, r)) & m;
+      cb[j] = ((BDUAL && r >= C::BN / 2 ? word(2, r - C::BN / 2) : word(1, r)) & m) >> (8 * g);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      // lane (g, m): scale of block 2 ks + g of its row (byte 2 ks + g of the row's word)
-      const int sh = 8 * (2 * ks + g);
+    for (int ks = 0; ks < NSL; ++ks) {
       i32x8 a[C::TM], b[C::TN];
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) a[i] = mx_frag(as, wm * C::WTM + i * 32 + (lane & 31), ks, g);
+      for (int i = 0; i < C::TM; ++i) a[i] = mx_frag<BK>(as, wm * C::WTM + i * 32 + (lane & 31), ks, g);
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) b[j] = mx_frag(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g);
+      for (int j = 0; j < C::TN; ++j) b[j] = mx_frag<BK>(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[i], b[j], acc[i][j], 0, 0, 0, static_cast<int>((ca[i] >> sh) & 0xFFu), 0,
-              static_cast<int>((cb[j] >> sh) & 0xFFu));
+        for (int j = 0; j < C::TN; ++j) {
+          const int sa = static_cast<int>(ca[i]), sb = static_cast<int>(cb[j]);
+          // TR: the tile transposed (B in the first operand slot), so a lane holds four consecutive output
+          // columns of one row (the register-direct and wave-staged epilogues)
+          if (ks == 0)
+            acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, sb, 0, sa)
+                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa, 0, sb);
+          else
+            acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 2, sb, 2, sa)
+                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 2, sa, 2, sb);
+        }
     }
   }
   __syncthreads();  // the epilogue reuses the LDS
@@ -239,11 +293,17 @@ struct MxArgs {
 };
 
 template <class C, int KIND>
-__global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_mx_kernel(MxArgs m) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLds];
   uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
   const FfnArgs& p = m.f;
   const int tid = threadIdx.x;
+  // 256 x 256 tiles on 8 waves of 128 x 64: computed transposed; G1 and G2 store from registers, the others
+  // through 8 KB of LDS per wave (whole-line stores); smaller tiles stage the whole tile in LDS
+  constexpr bool TR = C::BM == 256 && C::BN == 256 && C::kWaves == 8 && C::WTN == 64;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  uint16_t* wbuf = lds + wave * 4096;  // this wave's 8 KB of the (then idle) LDS
   const int d = p.d, f = p.f;
   const int64_t wsz = static_cast<int64_t>(d) * f;
   Acc<C> acc;
@@ -266,17 +326,19 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
       const int64_t so = e * wsz / 32 + static_cast<int64_t>(n0) * 4;  // scales grouped per expert over f rows
       const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, d, 0, d, kNoSplit, f - n0,
                    static_cast<int64_t>(f) * 4};
-      mx_mainloop<C, true>(a, b, d, lds8, tid, acc);
-      epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
+      mx_mainloop<C, true, TR>(a, b, d, lds8, tid, acc);
+      if constexpr (TR) epi_regs_swiglu_fwd<C>(acc, p, row0, rows, n0, lane, wm, wn);
+      else epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else if constexpr (KIND == kG2) {
       const int n0 = nt * C::BN;  // over d
       const MxKc a{m.aq + row0 * f, nullptr, m.as + row0 * 4, nullptr, f, 0, f, kNoSplit, rows, p.R * 4};
       const int64_t wo = e * wsz + static_cast<int64_t>(n0) * f;  // transposed Wd: [E][d][f]
       const int64_t so = e * wsz / 32 + static_cast<int64_t>(n0) * 4;  // scales grouped per expert over d rows
       const MxKc b{m.wdq + wo, nullptr, m.wds + so, nullptr, f, 0, f, kNoSplit, d - n0, static_cast<int64_t>(d) * 4};
-      mx_mainloop<C, false>(a, b, f, lds8, tid, acc);
+      mx_mainloop<C, false, TR>(a, b, f, lds8, tid, acc);
       // Y is read by the combine right after: ordinary (cached) stores
-      epi_store<C, false>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
+      if constexpr (TR) epi_regs_store<C>(acc, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, lane, wm, wn);
+      else epi_store<C, false>(acc, lds, static_cast<uint16_t*>(p.o_y) + row0 * d + n0, d, rows, d - n0, tid);
     } else if constexpr (KIND == kG3) {
       const int n0 = nt * C::BN;  // over f
       const MxKc a{m.dyq + row0 * d, nullptr, m.dys + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, p.R * 4};
@@ -294,14 +356,20 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
       const int64_t so = (static_cast<int64_t>(e) * d + n0) * 4;  // scales grouped over all E*d rows
       const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, f, 0, 2 * f, f, d - n0,
                    static_cast<int64_t>(p.E) * d * 4};
-      mx_mainloop<C, false>(a, b, 2 * f, lds8, tid, acc);
-      epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
+      mx_mainloop<C, false, TR>(a, b, 2 * f, lds8, tid, acc);
+      // dX rows are read by the dispatch backward right after: ordinary stores
+      if constexpr (TR)
+        epi_staged_store<C, false>(acc, wbuf, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, lane, wm,
+                                   wn);
+      else epi_store<C>(acc, lds, static_cast<uint16_t*>(p.o_dx) + row0 * d + n0, d, rows, d - n0, tid);
     }
   } else {  // weight gradients: K = 32-padded token blocks of expert e
     const int gm = KIND == kG4 ? (f + C::BM - 1) / C::BM : (d + C::BM - 1) / C::BM;
     const int gn = KIND == kG4 ? (d + C::BN - 1) / C::BN : 2 * ((f + C::BN - 1) / C::BN);
-    int e, mt, ntile;
-    if (!wgrad_tile(blockIdx.x, p.E, gm, gn, e, mt, ntile)) return;
+    int e, local;
+    if (!wgrad_tile_sorted(blockIdx.x, p.E, gm * gn, p.wsched, e, local)) return;
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int mt = local / gn, ntile = local % gn;
     const int b0 = __builtin_amdgcn_readfirstlane(m.blk[e]);
     const int64_t kb = static_cast<int64_t>(b0) * 32;
     const int K = (__builtin_amdgcn_readfirstlane(m.blk[e + 1]) - b0) * 32;
@@ -334,9 +402,272 @@ __global__ __launch_bounds__(C::kThreads) void ffn_mx_kernel(MxArgs m) {
       mvalid = d;
       nvalid = f;
     }
-    mx_mainloop<C, false>(a, b, K, lds8, tid, acc);
-    epi_store<C>(acc, lds, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0, tid);
+    mx_mainloop<C, false, TR>(a, b, K, lds8, tid, acc);
+    if constexpr (TR)
+      epi_staged_store<C, true>(acc, wbuf, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0,
+                                lane, wm, wn);
+    else epi_store<C>(acc, lds, Cp + static_cast<int64_t>(m0) * ldc + n0, ldc, mvalid - m0, nvalid - n0, tid);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent 256 x 256 MX kernel for the rows-by-expert GEMMs (G1, G2, G3, G5).
+// Workgroups loop over tiles (ids b, b + G, ... in the XCD-contiguous order),
+// and the K-steps of consecutive
+// tiles form one stream through the two LDS stages: each step's loads are
+// issued right after the barrier of the step before, and the last step of a
+// tile issues the next tile's first step, so those loads are in flight during
+// the epilogue.  Tiles are computed transposed (mfma(B, A)) so the epilogues run
+// from registers: G1 (SwiGLU) and G2 store straight from them; G3 stages its
+// Hg, Hu loads through both LDS stages (the next tile then starts after its
+// epilogue); G5 stages its rows through the stage the last step released for
+// whole-line stores.  (The weight gradients keep one workgroup per tile: a new
+// workgroup's loads do not wait for the previous tile's 128 KB of dW stores,
+// which a persistent workgroup's single vmcnt counter would; measured 21%
+// slower persistent.)
+// ---------------------------------------------------------------------------
+struct MxTile {
+  MxKc a, b;
+  int K;            // contraction length (0: zero outputs)
+  int rows, cols;   // valid output rows / columns from the tile origin
+  int64_t row0;     // rows-by-expert GEMMs: first row of the tile
+  int n0;           // first output column (over f for G1 and G3)
+  uint16_t* out;    // plain-store GEMMs: output tile origin
+  int64_t ldo;      // and its row stride
+};
+
+// Tile of hardware-order id `id` over the live table entries times the N
+// tiles (rows-by-expert GEMMs).  False past the last tile.
+template <class C, int KIND>
+__device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t live, MxTile& t) {
+  const FfnArgs& p = m.f;
+  const int d = p.d, f = p.f;
+  const int64_t wsz = static_cast<int64_t>(d) * f;
+  static_assert(KIND == kG1 || KIND == kG2 || KIND == kG3 || KIND == kG5, "rows-by-expert GEMMs");
+  {
+    const int gx = KIND == kG1 ? (f + C::BN / 2 - 1) / (C::BN / 2)
+                               : KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
+    const int64_t lid = xcd_tile(id, live * gx);
+    if (lid < 0) return false;
+    const int4 tt = p.tiles[lid / gx];
+    const int e = __builtin_amdgcn_readfirstlane(tt.x);
+    const int rows = e < 0 ? 0 : __builtin_amdgcn_readfirstlane(tt.z);
+    const int64_t row0 = e < 0 ? 0 : __builtin_amdgcn_readfirstlane(tt.y);
+    const int64_t ee = e < 0 ? 0 : e;
+    const int nt = static_cast<int>(lid % gx);
+    const int64_t R = p.R;
+    t.row0 = row0;
+    t.rows = rows;
+    if constexpr (KIND == kG1) {
+      t.n0 = nt * (C::BN / 2);
+      t.a = MxKc{m.xq + row0 * d, nullptr, m.xs + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, R * 4};
+      const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * d;      // transposed Wg, Wu: [E][f][d]
+      const int64_t so = ee * wsz / 32 + static_cast<int64_t>(t.n0) * 4;  // scales grouped per expert over f rows
+      t.b = MxKc{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, d, 0, d, kNoSplit, f - t.n0,
+                 static_cast<int64_t>(f) * 4};
+      t.K = d;
+      t.cols = f - t.n0;
+    } else if constexpr (KIND == kG2) {
+      t.n0 = nt * C::BN;  // over d
+      t.a = MxKc{m.aq + row0 * f, nullptr, m.as + row0 * 4, nullptr, f, 0, f, kNoSplit, rows, R * 4};
+      const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * f;      // transposed Wd: [E][d][f]
+      const int64_t so = ee * wsz / 32 + static_cast<int64_t>(t.n0) * 4;  // scales grouped per expert over d rows
+      t.b = MxKc{m.wdq + wo, nullptr, m.wds + so, nullptr, f, 0, f, kNoSplit, d - t.n0, static_cast<int64_t>(d) * 4};
+      t.K = f;
+      t.cols = d - t.n0;
+      t.out = static_cast<uint16_t*>(p.o_y) + row0 * d + t.n0;
+      t.ldo = d;
+    } else if constexpr (KIND == kG3) {
+      t.n0 = nt * C::BN;  // over f
+      t.a = MxKc{m.dyq + row0 * d, nullptr, m.dys + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, R * 4};
+      const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * d;    // natural Wd: [E][f][d]
+      const int64_t so = (ee * f + t.n0) * 4;                           // scales grouped over all E*f rows
+      t.b = MxKc{m.wdq + wo, nullptr, m.wds + so, nullptr, d, 0, d, kNoSplit, f - t.n0,
+                 static_cast<int64_t>(p.E) * f * 4};
+      t.K = d;
+      t.cols = f - t.n0;
+    } else {  // kG5
+      t.n0 = nt * C::BN;  // over d
+      t.a = MxKc{m.dhgq + row0 * f, m.dhuq + row0 * f, m.dhgs + row0 * 4, m.dhus + row0 * 4, f, 0, 2 * f, f, rows,
+                 R * 4};
+      const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * f;    // natural Wg, Wu: [E][d][f]
+      const int64_t so = (ee * d + t.n0) * 4;                           // scales grouped over all E*d rows
+      t.b = MxKc{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, f, 0, 2 * f, f, d - t.n0,
+                 static_cast<int64_t>(p.E) * d * 4};
+      t.K = 2 * f;
+      t.cols = d - t.n0;
+      t.out = static_cast<uint16_t*>(p.o_dx) + row0 * d + t.n0;
+      t.ldo = d;
+    }
+    if (rows == 0) t.K = 0;
+  }
+  return true;
+}
+
+// Whether hardware-order id `id` names a tile (as mx_tile, without building it).
+template <class C, int KIND>
+__device__ __forceinline__ bool mx_tile_valid(const FfnArgs& p, int64_t id, int64_t live) {
+  const int gx = KIND == kG1 ? (p.f + C::BN / 2 - 1) / (C::BN / 2)
+                             : KIND == kG3 ? (p.f + C::BN - 1) / C::BN : (p.d + C::BN - 1) / C::BN;
+  return xcd_tile(id, live * gx) >= 0;
+}
+
+template <class C, int KIND>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kWaves / 4)))
+void ffn_mx_persistent(MxArgs m) {
+  static_assert(C::BM == 256 && C::BN == 256 && C::kWaves == 8 && C::TM == 4 && C::WTN == 64,
+                "256 x 256 tiles on 8 waves of 128 x 64");
+  constexpr bool BDUAL = KIND == kG1;
+  constexpr bool kStaged = KIND == kG3;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLds];
+  uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
+  const FfnArgs& p = m.f;
+  const int tid = threadIdx.x, lane = tid & 63, g32 = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int64_t live = __builtin_amdgcn_readfirstlane(p.tiles[p.max_tiles].x);
+  const int64_t step = gridDim.x;
+  int64_t id = blockIdx.x;
+  MxTile cur;
+  if (!mx_tile<C, KIND>(m, id, live, cur)) return;
+
+  uint8_t* const qa = l8;                          // A stages
+  uint8_t* const qb = l8 + 2 * C::kA;              // B stages
+  uint8_t* const sl = l8 + 2 * C::kA + 2 * C::kB;  // scale stages: [2 groups][A 1 KB | B 2 KB]
+  constexpr int BH = BDUAL ? C::BN / 2 : C::BN;
+  // this wave's 8 KB of stage `slot` (bf16 elements) for the staged epilogues
+  auto stage_buf = [&](int slot) -> uint16_t* {
+    return reinterpret_cast<uint16_t*>(wave < 4 ? qa + slot * C::kA + wave * 8192
+                                                : qb + slot * C::kB + (wave - 4) * 8192);
+  };
+  // step kt of tile t into stage `slot`: the A and B tiles and the scale runs (one per wave:
+  // group (0, 1) x {A, B half 0, B half 1}; group 1 only for K-steps that straddle two groups)
+  auto issue = [&](const MxTile& t, int kt, int slot) {
+    const int k0 = kt * C::BK;
+    mx_dma<C, C::BM, false>(t.a, k0, qa + slot * C::kA, wave, lane);
+    mx_dma<C, C::BN, BDUAL>(t.b, k0, qb + slot * C::kB, wave, lane);
+    const int o = static_cast<int>((t.a.k_base / 32) & 3);
+    const int grp = wave / 3, part = wave % 3;
+    if (wave < 6 && !(grp == 1 && o == 0) && !(part == 2 && !BDUAL)) {
+      const int arows = t.a.mn_valid < C::BM ? t.a.mn_valid : C::BM;
+      const int brows = t.b.mn_valid < BH ? t.b.mn_valid : BH;
+      const bool hi = !BDUAL && k0 >= t.a.ksplit;
+      const int kk = hi ? k0 - t.a.ksplit : k0;
+      const int64_t G = (t.a.k_base / 32 + kk / 32) >> 2;
+      uint8_t* dst = sl + slot * C::kScaleStage + grp * 3072 + part * 1024;
+      if (part == 0)
+        scale_dma(hi ? t.a.s1 : t.a.s0, t.a.gs, G + grp, arows, dst, lane);
+      else
+        scale_dma((part == 2 || (!BDUAL && hi)) ? t.b.s1 : t.b.s0, t.b.gs, G + grp, brows, dst, lane);
+    }
+  };
+
+  int g = 0;         // stage position of the current tile's step 0
+  bool pre = false;  // the current tile's step 0 already issued
+  for (;;) {
+    const int64_t nid = id + step;
+    const bool more = mx_tile_valid<C, KIND>(p, nid, live);
+    const int nk = (cur.K + C::BK - 1) / C::BK;
+    if (!pre && nk > 0) issue(cur, 0, g & 1);
+    const int o = static_cast<int>((cur.a.k_base / 32) & 3);
+    Acc<C> acc;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm<0>();
+      __syncthreads();
+      const int slot = (g + kt) & 1;
+      // the next step's loads into the other stage: this tile's, or at its last step the next tile's first
+      if (kt + 1 < nk) {
+        issue(cur, kt + 1, slot ^ 1);
+      } else if (kStaged) {
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 0, stage_buf(slot ^ 1), wm, wn, lane);
+      } else if (more) {
+        MxTile t2;
+        mx_tile<C, KIND>(m, nid, live, t2);
+        if (t2.K > 0) issue(t2, 0, slot ^ 1);
+      }
+      const uint8_t* as = qa + slot * C::kA;
+      const uint8_t* bs = qb + slot * C::kB;
+      const uint8_t* ss = sl + slot * C::kScaleStage;
+      // bytes of this step's four blocks that lie inside the tile's K range
+      const int nb = (cur.a.k_valid - kt * C::BK) / 32;
+      const uint32_t msk = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
+      auto word = [&](int part, int row) -> uint32_t {
+        const uint32_t w0 = reinterpret_cast<const uint32_t*>(ss + part * 1024)[row];
+        if (o == 0) return w0;
+        const uint32_t w1 = reinterpret_cast<const uint32_t*>(ss + 3072 + part * 1024)[row];
+        return (w0 >> (8 * o)) | (w1 << (32 - 8 * o));
+      };
+      // lane (g, m): block 2 ks + g of its row at byte 2 ks of the word shifted down by g bytes (op_sel)
+      uint32_t ca[C::TM], cb[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) ca[i] = (word(0, wm * C::WTM + i * 32 + (lane & 31)) & msk) >> (8 * g32);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int r = b_row<C, BDUAL>(wn, j) + (lane & 31);
+        cb[j] = ((BDUAL && r >= C::BN / 2 ? word(2, r - C::BN / 2) : word(1, r)) & msk) >> (8 * g32);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        i32x8 a[C::TM], b[C::TN];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) a[i] = mx_frag<C::BK>(as, wm * C::WTM + i * 32 + (lane & 31), ks, g32);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) b[j] = mx_frag<C::BK>(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g32);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = ks == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                      b[j], a[i], acc[i][j], 0, 0, 0, static_cast<int>(cb[j]), 0, static_cast<int>(ca[i]))
+                                : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                      b[j], a[i], acc[i][j], 0, 0, 2, static_cast<int>(cb[j]), 2, static_cast<int>(ca[i]));
+      }
+    }
+    pre = nk > 0 && !kStaged && more;
+    g += nk;
+    if constexpr (kStaged) {
+      // blocks 0, 1 in the two stage buffers, then 2, 3; block 0 was issued at the last K-step
+      if (nk > 0) {
+        uint16_t* b0 = stage_buf(g & 1);
+        uint16_t* b1 = stage_buf((g + 1) & 1);
+        __syncthreads();  // the last step's stage is free
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 1, b1, wm, wn, lane);
+        wait_vm<0>();
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 0, b0, wm, wn, lane);
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 1, b1, wm, wn, lane);
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 2, b0, wm, wn, lane);
+        g3_stage<C>(p, cur.row0, cur.rows, cur.n0, 3, b1, wm, wn, lane);
+        wait_vm<0>();
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 2, b0, wm, wn, lane);
+        g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 3, b1, wm, wn, lane);
+        __syncthreads();  // the LDS holds stages again
+      }
+    } else if constexpr (KIND == kG5) {
+      if (nk > 0) __syncthreads();  // the last step's stage is free
+      // dX rows are read by the dispatch backward right after: ordinary stores
+      epi_staged_store<C, false>(acc, stage_buf((g + 1) & 1), cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
+    } else if constexpr (KIND == kG1) {
+      epi_regs_swiglu_fwd<C>(acc, p, cur.row0, cur.rows, cur.n0, lane, wm, wn);
+    } else {  // G2: Y is read by the combine right after: ordinary stores
+      epi_regs_store<C>(acc, cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
+    }
+    if (!more) break;
+    mx_tile<C, KIND>(m, nid, live, cur);
+    id = nid;
+  }
+}
+
+template <int KIND>
+void launch_mx_persistent(const char* name, const MxArgs& a, int64_t tiles, hipStream_t s) {
+  using C = MxBigP;
+  static const int occ = occupancy(reinterpret_cast<const void*>(&ffn_mx_persistent<C, KIND>), C::kThreads);
+  MOE_LAUNCH(name, (ffn_mx_persistent<C, KIND>), dim3(persistent_grid(occ, tiles)), dim3(C::kThreads), 0, s, a);
 }
 
 template <class C>
@@ -351,11 +682,13 @@ int launch_mx_cfg(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
     case kG3: MOE_LAUNCH("G3_mx", (ffn_mx_kernel<C, kG3>), dim3(xcd_grid(nf * max_tiles)), blk, 0, s, a); break;
     case kG5: MOE_LAUNCH("G5_mx", (ffn_mx_kernel<C, kG5>), dim3(xcd_grid(nd * max_tiles)), blk, 0, s, a); break;
     case kG4:
-      MOE_LAUNCH("G4_mx", (ffn_mx_kernel<C, kG4>), dim3(static_cast<unsigned>(a.f.E * cdiv(a.f.f, C::BM) * nd)), blk,
+      MOE_LAUNCH("G4_mx", (ffn_mx_kernel<C, kG4>),
+                 dim3(static_cast<unsigned>(wgrad_sorted_grid(a.f.E, static_cast<int>(cdiv(a.f.f, C::BM) * nd)))), blk,
                  0, s, a);
       break;
     case kG6:
-      MOE_LAUNCH("G6_mx", (ffn_mx_kernel<C, kG6>), dim3(static_cast<unsigned>(a.f.E * cdiv(a.f.d, C::BM) * 2 * nf)),
+      MOE_LAUNCH("G6_mx", (ffn_mx_kernel<C, kG6>),
+                 dim3(static_cast<unsigned>(wgrad_sorted_grid(a.f.E, static_cast<int>(cdiv(a.f.d, C::BM) * 2 * nf)))),
                  blk, 0, s, a);
       break;
     default: return MOE_EINVAL;
@@ -366,10 +699,22 @@ int launch_mx_cfg(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
 bool mx_big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 512; }
 bool mx_big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
 
+// 256 x 256 tiles: the SwiGLU-backward GEMM (G3) on the persistent kernel, the
+// others one workgroup per tile.  Measured on the MXFP8 E = 128 workload: G3
+// persistent 763-770 us against 840 on its own 128-row table; G1, G2, G5
+// persistent 1189-1322, 679-708, 1260-1322 us against 1176-1198, 695, 1237-1240
+// per tile (their epilogues store from registers either way, so a persistent
+// workgroup gains little, and the next tile's state costs registers).
 int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
+  using C = MxBig;
   const bool wgrad = kind == kG4 || kind == kG6;
-  const bool big = wgrad ? mx_big_wgrad(a.f) : a.f.bm == MxBig::BM;
-  return big ? launch_mx_cfg<MxBig>(kind, a, max_tiles, s) : launch_mx_cfg<MxSmall>(kind, a, max_tiles, s);
+  const bool big = wgrad ? mx_big_wgrad(a.f) : a.f.bm == C::BM;
+  if (!big) return launch_mx_cfg<MxSmall>(kind, a, max_tiles, s);
+  if (kind == kG3) {
+    launch_mx_persistent<kG3>("G3_mx", a, cdiv(a.f.f, C::BN) * max_tiles, s);
+    return launch_status();
+  }
+  return launch_mx_cfg<C>(kind, a, max_tiles, s);
 }
 
 // Scratch carving: a bump allocator over the caller's workspace.
@@ -540,15 +885,7 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
     if (!dy_mx) launch_mx_rows(a.dy, bf, a.R, a.d, b.dy.q, b.dy.s, s, true);
     m.dyq = dy_mx ? dy_mx : b.dy.q;
     m.dys = dy_mx ? dy_mx + align_up(static_cast<size_t>(a.R) * a.d, 256) : b.dy.s;
-    if (a.tiles128) {  // 128 x 128 tiles for the SwiGLU backward
-      MxArgs m3 = m;
-      m3.f.tiles = a.tiles128;
-      m3.f.max_tiles = a.max_tiles128;
-      m3.f.bm = 128;
-      st = launch_mx_kind(kG3, m3, a.max_tiles128, s);
-    } else {
-      st = launch_mx_kind(kG3, m, max_tiles, s);
-    }
+    st = launch_mx_kind(kG3, m, max_tiles, s);
     if (st != MOE_OK) return st;
     // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f
     launch_mx_rows(a.dhg, bf, a.R, a.f, b.dhg.q, b.dhg.s, s, true);
