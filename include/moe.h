@@ -236,9 +236,19 @@ int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, co
  * w_down [E, f, d] (bf16) in both orientations the MXFP8 FFN uses (forward:
  * blocks along d for w_gate/w_up and along f for w_down; backward: blocks along
  * the last axis), each produced from a single read of the weight.
- * moe_mx_weight_cache_bytes(E, d, f) = 6 E d f (1 + 1/32) bytes plus alignment;
- * the layout is internal (hand the cache back to moe_grouped_ffn_fwd/_bwd
- * unchanged).  The cache stays valid while the weights are unchanged; building
+ * moe_mx_weight_cache_bytes(E, d, f) = 6 E d f (1 + 1/32) bytes plus alignment.
+ * Layout (the FFN calls take the cache back unchanged; it is stated so that it
+ * can be inspected or stored): six regions in the order w_gate, w_up, w_down
+ * forward, then w_gate, w_up, w_down backward; each region is its E4M3 codes
+ * (E d f bytes) and then its E8M0 scale bytes (E d f / 32), both parts starting
+ * on a 256-byte boundary.  A forward region holds each expert's weight
+ * quantised down its rows and stored transposed ([E, f, d] for w_gate/w_up,
+ * [E, d, f] for w_down; blocks run along the last axis); with M the rows and
+ * K the last axis of that stored form, the scale of expert e, row m, block b
+ * is byte e M (K/32) + ((b/4) M + m) 4 + b%4.  A backward region keeps the
+ * weight's own shape with blocks along its last axis, and the scale of expert
+ * e, row m, block b is byte ((b/4) E M + e M + m) 4 + b%4.  The cache stays
+ * valid while the weights are unchanged; building
  * again overwrites it.  Errors: MOE_EINVAL (null or unaligned pointer, bad E,
  * d, f), MOE_EUNSUPPORTED (d or f not a multiple of 128), MOE_EWORKSPACE
  * (cache_bytes too small); nothing is launched then. */

@@ -131,6 +131,20 @@ constexpr int kMaxK = 8;
 // reads soon: they stream to memory instead of being allocated (and filled) in
 // the L2.  Measured faster for the dispatch rows and the GEMM epilogues, slower
 // for the combine outputs, which keep ordinary stores.
+// Read of a value the whole wave shares (tile tables, expert schedules) through
+// the constant address space, so that the compiler issues a scalar load (counted
+// by lgkmcnt): a vector load would sit in the vector memory counter behind the
+// wave's earlier stores, and waiting for it would wait for them.  Only for data
+// no kernel in flight writes.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+__device__ __forceinline__ int4 ld_uniform(const int4* p) {
+  typedef int i32x4_c __attribute__((ext_vector_type(4)));
+  const i32x4_c v = *(const __attribute__((address_space(4))) i32x4_c*)p;
+  return make_int4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 w = {v.x, v.y, v.z, v.w};

@@ -53,11 +53,18 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
       const int64_t r0 = off_s[e] + i * BM;
       int64_t rows = n_s[e] - i * BM < BM ? n_s[e] - i * BM : BM;
       if (r0 + rows > R) rows = R - r0 > 0 ? R - r0 : 0;  // memory safety against bad offsets
-      t = make_int4(rows > 0 ? e : -1, static_cast<int>(r0), static_cast<int>(rows), 0);
+      t = make_int4(rows > 0 ? e : -1, static_cast<int>(r0), static_cast<int>(rows), e);
     }
     tiles[slot] = t;
   }
   if (tid == 0) tiles[max_tiles] = make_int4(static_cast<int>(used), 0, 0, 0);
+  // each expert's run of entries, cut at the live count
+  if (tid < E) {
+    const int64_t first = cum[tid] - cnt;
+    int64_t n = used - first < cnt ? used - first : cnt;
+    if (n < 0) n = 0;
+    tiles[max_tiles + 1 + tid] = make_int4(static_cast<int>(first), static_cast<int>(n), 0, 0);
+  }
 }
 
 // One workgroup: each expert's cost, then its rank (the number of experts
@@ -106,7 +113,8 @@ size_t elem_bytes(int prec) { return prec == MOE_F32 ? 4 : 2; }
 // Workspace layout: [tile table][experts sorted by weight-gradient cost][dHg][dHu] (backward only)[MX scratch]
 // (MXFP8 only).
 size_t tiles_bytes(const FfnShape& s) {
-  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec, s.R, s.E)) + 1) * sizeof(int4), 256);
+  return align_up(static_cast<size_t>(max_m_tiles(s.R, s.E, tile_bm(s.prec, s.R, s.E)) + 1 + kMaxE) * sizeof(int4),
+                  256);
 }
 
 size_t ffn_ws_bytes(const FfnShape& s, int is_bwd) {

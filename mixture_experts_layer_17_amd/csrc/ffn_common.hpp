@@ -23,8 +23,9 @@ enum FfnKind { kG1 = 1, kG2 = 2, kG3 = 3, kG4 = 4, kG5 = 5, kG6 = 6 };
 
 struct FfnArgs {
   const int32_t* offsets;  // [E+1] expert segment offsets (device)
-  const int4* tiles;       // M-tile table: {expert, row0, rows, 0}; expert < 0 past the end;
-                           // entry [max_tiles] = {number of live tiles, 0, 0, 0}
+  const int4* tiles;       // M-tile table: {expert (< 0: no rows), row0, rows, expert}, expert < 0 past
+                           // the end; entry [max_tiles] = {number of live tiles, 0, 0, 0}; entry
+                           // [max_tiles + 1 + e] = {first entry of expert e, its number of entries, 0, 0}
   int64_t max_tiles;
   int bm;                  // row-tile height the tile table was built for
   const int32_t* wsched;   // backward: the experts sorted by weight-gradient cost (wgrad_tile_sorted)
@@ -55,6 +56,27 @@ inline unsigned xcd_grid(int64_t total) {
   return static_cast<unsigned>(cdiv(total, kNumXcd) * kNumXcd);
 }
 
+// Rows-by-expert tile order over the live entries of the tile table times gx
+// column tiles: each expert's run of entries [T, T + n) is taken in pairs of
+// row tiles, and inside a pair the column tile is the major index, so the two
+// row tiles that read the same weight columns take consecutive logical ids
+// (hence, through xcd_tile, CUs of one XCD at about the same time) and fetch
+// those columns into its L2 once, while an expert with many row tiles still
+// works on few of them at a time (its X rows stay in L2 too).  Returns the
+// table entry and the column tile of logical id lid (< live * gx).
+__device__ __forceinline__ int64_t expert_tile(int64_t lid, int gx, const int4* tiles, int64_t max_tiles, int& nt) {
+  const int e = __builtin_amdgcn_readfirstlane(ld_uniform(tiles + lid / gx).w);
+  const int4 run = ld_uniform(tiles + max_tiles + 1 + e);
+  const int64_t first = __builtin_amdgcn_readfirstlane(run.x);
+  const int n = __builtin_amdgcn_readfirstlane(run.y);
+  const int64_t l = lid - first * gx;
+  const int64_t pair = l / (2 * gx);
+  const int m = n - 2 * pair < 2 ? 1 : 2;  // row tiles in this pair (the last of an odd run has one)
+  const int64_t l2 = l - pair * 2 * gx;
+  nt = static_cast<int>(l2 / m);
+  return first + 2 * pair + l2 % m;
+}
+
 // Weight-gradient tile order for one workgroup per tile (G4, G6), from the
 // experts sorted by cost (sched[0, E), as launch_wgrad_sched writes it).  The
 // hardware deals workgroup ids round-robin over the 8 XCDs; id h runs on XCD
@@ -79,7 +101,7 @@ __device__ __forceinline__ bool wgrad_tile_sorted(int64_t h, int E, int ntile, c
     local = static_cast<int>(q - static_cast<int64_t>(r) * ntile);
   }
   if (j >= E) return false;
-  e = sched[j];
+  e = ld_uniform(sched + __builtin_amdgcn_readfirstlane(j));
   return true;
 }
 inline int64_t wgrad_sorted_grid(int E, int ntile) {

@@ -268,19 +268,19 @@ __device__ __forceinline__ bool make_tile(const FfnArgs& p, int64_t h, int64_t l
   const uint16_t* Wu = static_cast<const uint16_t*>(p.wu);
   const uint16_t* Wd = static_cast<const uint16_t*>(p.wd);
   if constexpr (KIND == kG1 || KIND == kG2 || KIND == kG3 || KIND == kG5) {
-    // logical tile = (row tile, N tile), N tile fastest
+    // logical tile = (row tile, N tile) in the expert column-major order (expert_tile)
     const int gx = KIND == kG1 ? (f + C::BN / 2 - 1) / (C::BN / 2)
                                : KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
     const int64_t lid = xcd_tile(h, live * gx);
     if (lid < 0) return false;
-    const int4 tt = p.tiles[lid / gx];
+    int nt;
+    const int4 tt = p.tiles[expert_tile(lid, gx, p.tiles, p.max_tiles, nt)];
     // tile-table values are workgroup-uniform: keep them (and the buffer
     // descriptors built from them) in scalar registers
     const int e = __builtin_amdgcn_readfirstlane(tt.x);
     const int rows = e < 0 ? 0 : __builtin_amdgcn_readfirstlane(tt.z);
     const int64_t row0 = e < 0 ? 0 : __builtin_amdgcn_readfirstlane(tt.y);
     const int64_t eo = e < 0 ? 0 : static_cast<int64_t>(e) * wsz;
-    const int nt = static_cast<int>(lid % gx);
     t.row0 = row0;
     t.rows = rows;
     if constexpr (KIND == kG1) {

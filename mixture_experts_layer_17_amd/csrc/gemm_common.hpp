@@ -55,12 +55,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_dst, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_dst), 16, voff, 0, 0, 0);
 }
 
-// Wait until at most N LDS-DMA loads of this wave are outstanding (N < 16;
-// expcnt and lgkmcnt left alone).  Loads complete in issue order.
+// Wait until at most N vector memory operations of this wave are outstanding
+// (N < 64: the counter's low four bits sit in bits 3:0 of the immediate, its
+// high two in bits 15:14; expcnt and lgkmcnt left alone).  On this
+// architecture loads and stores share the counter and retire in issue order.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // ---------------------------------------------------------------------------

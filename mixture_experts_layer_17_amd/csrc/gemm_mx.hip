@@ -313,11 +313,11 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
                                : KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
     const int64_t lid = xcd_tile(blockIdx.x, static_cast<int64_t>(p.tiles[p.max_tiles].x) * gx);
     if (lid < 0) return;
-    const int4 t = p.tiles[lid / gx];
+    int nt;
+    const int4 t = p.tiles[expert_tile(lid, gx, p.tiles, p.max_tiles, nt)];
     if (t.x < 0) return;
     const int e = __builtin_amdgcn_readfirstlane(t.x), rows = __builtin_amdgcn_readfirstlane(t.z);
     const int64_t row0 = __builtin_amdgcn_readfirstlane(t.y);
-    const int nt = static_cast<int>(lid % gx);
     if constexpr (KIND == kG1) {
       const int n0 = nt * (C::BN / 2);
       const int64_t R = p.R;
@@ -370,9 +370,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (!wgrad_tile_sorted(blockIdx.x, p.E, gm * gn, p.wsched, e, local)) return;
     e = __builtin_amdgcn_readfirstlane(e);
     const int mt = local / gn, ntile = local % gn;
-    const int b0 = __builtin_amdgcn_readfirstlane(m.blk[e]);
+    const int b0 = __builtin_amdgcn_readfirstlane(ld_uniform(m.blk + e));
     const int64_t kb = static_cast<int64_t>(b0) * 32;
-    const int K = (__builtin_amdgcn_readfirstlane(m.blk[e + 1]) - b0) * 32;
+    const int K = (__builtin_amdgcn_readfirstlane(ld_uniform(m.blk + e + 1)) - b0) * 32;
     const int m0 = mt * C::BM;
     uint16_t* Cp;
     int n0, ldc, mvalid, nvalid;
@@ -449,12 +449,12 @@ __device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t liv
                                : KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
     const int64_t lid = xcd_tile(id, live * gx);
     if (lid < 0) return false;
-    const int4 tt = p.tiles[lid / gx];
+    int nt;
+    const int4 tt = ld_uniform(p.tiles + expert_tile(lid, gx, p.tiles, p.max_tiles, nt));
     const int e = __builtin_amdgcn_readfirstlane(tt.x);
     const int rows = e < 0 ? 0 : __builtin_amdgcn_readfirstlane(tt.z);
     const int64_t row0 = e < 0 ? 0 : __builtin_amdgcn_readfirstlane(tt.y);
     const int64_t ee = e < 0 ? 0 : e;
-    const int nt = static_cast<int>(lid % gx);
     const int64_t R = p.R;
     t.row0 = row0;
     t.rows = rows;
@@ -525,7 +525,7 @@ void ffn_mx_persistent(MxArgs m) {
   const int tid = threadIdx.x, lane = tid & 63, g32 = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int64_t live = __builtin_amdgcn_readfirstlane(p.tiles[p.max_tiles].x);
+  const int64_t live = __builtin_amdgcn_readfirstlane(ld_uniform(p.tiles + p.max_tiles).x);
   const int64_t step = gridDim.x;
   int64_t id = blockIdx.x;
   MxTile cur;

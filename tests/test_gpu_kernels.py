@@ -356,3 +356,63 @@ def test_mx_quantize_segments_bit_exact(gpu):
             b += 1
     assert b == len(rs)
     assert np.all(q[:, 32 * b:] == 0) and np.all(s[:, b:] == 0)   # padding past the last segment
+
+
+def _wcache_regions(E, d, f):
+    """Byte ranges of the weight cache as its header documents them: six regions
+    (w_gate, w_up, w_down forward, then the same three backward), each the E4M3
+    codes followed by the scale bytes, every part starting on a 256-byte boundary."""
+    up = lambda n: -(-n // 256) * 256
+    n, off, out = E * d * f, 0, []
+    for _ in range(6):
+        out.append((off, off + n, off + up(n), off + up(n) + n // 32))
+        off += up(n) + up(n // 32)
+    return out, off
+
+
+def _wcache_check(cache, reg, wts, E, forward):
+    """One region against the oracle: forward codes are each expert's weight
+    quantised down its rows and stored transposed, scales grouped per expert
+    ([K/128][M][4] bytes, M = output rows, K = the blocked axis); backward codes
+    keep the weight's shape, blocks along its last axis, scales grouped over all
+    experts' rows ([K/128][E*M][4])."""
+    q0, q1, s0, s1 = reg
+    m_rows = wts.shape[2] if forward else wts.shape[1]
+    k_len = wts.shape[1] if forward else wts.shape[2]
+    codes = cache[q0:q1].reshape(E, m_rows, k_len)
+    sc = cache[s0:s1]
+    nb = k_len // 32
+    b = np.arange(nb)
+    for e in range(E):
+        rq, rs = mxo.mx_quantize(wts[e], axis=0 if forward else 1)
+        if forward:
+            np.testing.assert_array_equal(codes[e], rq.T)
+            m = np.arange(m_rows)[:, None]
+            idx = e * m_rows * nb + ((b[None, :] // 4) * m_rows + m) * 4 + b[None, :] % 4
+            np.testing.assert_array_equal(sc[idx], rs.T)          # rs [nb, M]
+        else:
+            np.testing.assert_array_equal(codes[e], rq)
+            m = np.arange(m_rows)[:, None]
+            idx = ((b[None, :] // 4) * E * m_rows + e * m_rows + m) * 4 + b[None, :] % 4
+            np.testing.assert_array_equal(sc[idx], rs)            # rs [M, nb]
+
+
+@pytest.mark.parametrize("E,d,f", [(3, 256, 384), (2, 128, 128), (1, 512, 256)])
+def test_mx_weight_cache_bit_exact(gpu, E, d, f):
+    """Both orientations of every weight in the cache (one read of each weight
+    feeds both) against the oracle's MX encoding, bit for bit, in the layout the
+    header documents; rows of very different magnitude share column blocks."""
+    gu.say(f"case mx weight cache E={E} d={d} f={f}")
+    wg, vg = _mx_input((E, d, f), 21, torch.bfloat16)
+    wu, vu = _mx_input((E, d, f), 22, torch.bfloat16)
+    wd, vd = _mx_input((E, f, d), 23, torch.bfloat16)
+    vg[0, :32, :32] = 0.0                                         # an all-zero block in both orientations
+    wg[0, :32, :32] = 0.0
+    regions, total = _wcache_regions(E, d, f)
+    assert B.lib().moe_mx_weight_cache_bytes(E, d, f) == total
+    cache = torch.full((total,), 0xFF, dtype=torch.uint8, device="cuda")
+    B.moe_mx_weight_cache_build(wg.cuda(), wu.cuda(), wd.cuda(), cache=cache)
+    torch.cuda.synchronize()
+    c = cache.cpu().numpy()
+    for i, (v, fwd) in enumerate([(vg, True), (vu, True), (vd, True), (vg, False), (vu, False), (vd, False)]):
+        _wcache_check(c, regions[i], v, E, fwd)
