@@ -87,20 +87,24 @@ def kernel_work(name: str, w, s: int) -> tuple[str, float]:
         "route_select": 4 * T * E + 12 * R,
         "route_topk_bwd": 8 * R + 4 * T * E + 4 * R,
     }
+    o = 1 + 1 / 32                              # bytes per MX element: E4M3 code + 1/32 of an E8M0 scale
+    rp = 128 * (-(-(-(-R // 32) + E) // 4) + 1)  # padded token axis of the token-axis MX layout
     if w.prec == "mxfp8":
-        # the dispatch and the combine backward also write the MX rows layout of x_perm / dy_perm
-        hbm["dispatch"] += R * d * (1 + 1 / 32)
-        hbm["combine_bwd"] += R * d * (1 + 1 / 32)
+        # the combine backward computes only dgates; X and dY go to their MX layouts through mx_gather
+        hbm["combine_bwd"] = T * d * s + R * d * s + 12 * R
+        # mx_gather, 2 launches (X, then dY = gate x dout): every expert row read from its token row (plus the
+        # permutation, and the gates for dY), written in the rows layout and in the token-axis layout
+        hbm["mx_gather"] = R * d * s + 6 * R + R * d * o + rp * d * o
     if name in hbm:
         return "hbm", float(hbm[name])
     if name == "mx_quantize_rows":
-        # A, dHg, dHu [R, f] along f, one launch each (X and dY come quantised from the dispatch and the combine
-        # backward); per element the source (s bytes) is read and 1 + 1/32 bytes written
-        return "hbm", float(R * f * (s + 1 + 1 / 32))
+        # A, dHg, dHu [R, f] along f, one launch each; per element the source (s bytes) is read and 1 + 1/32
+        # bytes written
+        return "hbm", float(R * f * (s + o))
     if name == "mx_quantize_cols":
-        # X and dY [R, d], A, dHg, dHu [R, f] down the tokens of each expert segment, transposed: 5 launches
-        elems = 2 * R * d + 3 * R * f
-        return "hbm", float(elems * (s + 1 + 1 / 32) / 5)
+        # A, dHg, dHu [R, f] down the tokens of each expert segment, transposed into the padded token axis:
+        # 3 launches
+        return "hbm", float(R * f * s + rp * f * o)
     if name == "mx_quantize_both":
         # one expert weight [E, d, f] per launch (3 per step): read once, written in both layouts
         return "hbm", float(E * d * f * (s + 2 * (1 + 1 / 32)))

@@ -62,6 +62,7 @@ typedef enum {
  * operands quantised on the device, fp32 accumulate). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_prec;
 
+/* 4: moe_grouped_ffn_bwd takes x_mxt and dy_mxt; the token-axis MX calls. */
 int moe_abi_version(void);
 const char* moe_status_str(int status);
 
@@ -191,6 +192,41 @@ int moe_combine_bwd_mx(const void* dout, const void* y_perm, const float* gates,
                        int64_t T, int32_t d, int32_t k, void* dy_perm, float* dgates, void* dy_mx,
                        void* stream);
 
+/* MXFP8 data movement with the token-axis layout ("Scaling and optimizing MoE
+ * training": the MXFP8 gains came from the expert FFN and from moving data
+ * between experts).  The weight gradients contract over each expert's tokens,
+ * so the MXFP8 backward needs X and dY also quantised along the tokens, per
+ * expert segment; these two calls write that layout together with the rows
+ * layout of moe_dispatch_mx / moe_combine_bwd_mx, from one destination-major
+ * pass that reads each expert row's token row directly, so the bf16 expert rows
+ * need not be written at all (x_perm / dy_perm may be NULL; given, they receive
+ * the same rows as moe_dispatch / moe_combine_bwd).
+ * Token-axis layout of an expert-major [R, cols] buffer (the MX buffer `*_mxt`,
+ * caller-owned, moe_mx_tok_bytes(R, E, cols) bytes): Rp = moe_mx_tok_rows(R, E)
+ * padded token positions, expert e's 32-row blocks at positions
+ * [32 mx_blk_offsets[e], 32 mx_blk_offsets[e+1]) (mx_blk_offsets from
+ * moe_route_topk; a segment's last block zero-padded, positions past the last
+ * segment zero); E4M3 codes [cols, Rp] (column c, position p at c Rp + p), then
+ * at the next 256-byte boundary the E8M0 bytes, the byte of (column c, block b)
+ * at ((b/4) cols + c) 4 + b%4.  Codes and scales are bit-identical to
+ * mx_quantize(axis 0, seg_offsets = offsets) of the bf16 expert rows (scales
+ * regrouped as stated).  The rows layout `*_mx` is as for moe_dispatch_mx.
+ * moe_combine_bwd_mx_tok also writes dgates (as moe_combine_bwd); dY = gate x
+ * dout is rounded to bf16 before it is encoded, as moe_combine_bwd stores it.
+ * perm_src, offsets, mx_blk_offsets: from moe_route_topk for the same T, E, k.
+ * bf16 only; d % 128 == 0 (else MOE_EUNSUPPORTED); 1 <= E <= 256; otherwise as
+ * moe_dispatch / moe_combine_bwd.  moe_mx_tok_rows / _bytes return 0 for
+ * invalid sizes. */
+int64_t moe_mx_tok_rows(int64_t R, int32_t E);
+size_t moe_mx_tok_bytes(int64_t R, int32_t E, int32_t cols);
+int moe_dispatch_mx_tok(const void* x, int64_t T, int32_t d, int32_t k, int32_t E, const int32_t* perm_src,
+                        const int32_t* offsets, const int32_t* mx_blk_offsets, void* x_perm, void* x_mx,
+                        void* x_mxt, void* stream);
+int moe_combine_bwd_mx_tok(const void* dout, const void* y_perm, const float* gates, const int32_t* perm_dst,
+                           const int32_t* perm_src, const int32_t* offsets, const int32_t* mx_blk_offsets,
+                           int64_t T, int32_t d, int32_t k, int32_t E, void* dy_perm, float* dgates, void* dy_mx,
+                           void* dy_mxt, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Grouped SwiGLU expert FFN ("Scaling and optimizing MoE training": the small
  * per-expert products run as one grouped GEMM; MXFP8 where it pays).
@@ -215,8 +251,14 @@ int moe_combine_bwd_mx(const void* dout, const void* y_perm, const float* gates,
  * validated); results are bit-identical to those without it.
  * x_mx (forward) / dy_mx (backward) (MOE_MXFP8 only, else MOE_EINVAL; may be
  * NULL): x_perm / dy_perm already in the MX rows layout written by
- * moe_dispatch_mx / moe_combine_bwd_mx for the same buffer; the call then does
- * not quantise it again (bit-identical results). */
+ * moe_dispatch_mx / moe_combine_bwd_mx (or the _tok calls) for the same buffer;
+ * the call then does not quantise it again (bit-identical results).
+ * x_mxt / dy_mxt (backward, MOE_MXFP8 only, else MOE_EINVAL; may be NULL): X / dY
+ * in the token-axis layout of moe_dispatch_mx_tok / moe_combine_bwd_mx_tok, used
+ * by the weight gradients instead of quantising x_perm / dy_perm along the
+ * tokens (bit-identical results).  With MOE_MXFP8, x_perm may be NULL when the
+ * forward has x_mx and the backward x_mxt, and dy_perm when the backward has
+ * both dy_mx and dy_mxt. */
 size_t moe_grouped_ffn_workspace(int64_t R, int32_t E, int32_t d, int32_t f, int prec, int is_bwd);
 int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, const int32_t* offsets,
                         const void* x_perm, const void* w_gate, const void* w_up, const void* w_down,
@@ -226,8 +268,8 @@ int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, int prec, co
                         const int32_t* mx_blk_offsets, const void* dy_perm, const void* x_perm,
                         const void* h_gate, const void* h_up, const void* a_act, const void* w_gate,
                         const void* w_up, const void* w_down, const void* mx_wcache, const void* dy_mx,
-                        void* dx_perm, void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
-                        void* stream);
+                        const void* x_mxt, const void* dy_mxt, void* dx_perm, void* dw_gate, void* dw_up,
+                        void* dw_down, void* ws, size_t ws_bytes, void* stream);
 
 /* Pre-quantised MXFP8 expert weights ("Scaling and optimizing MoE training":
  * converting into MXFP8 has a cost the savings must exceed).  Weights change

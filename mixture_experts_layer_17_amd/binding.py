@@ -41,8 +41,12 @@ _SIGS = {
                                _c_void_p, _c_void_p]),
     "moe_grouped_ffn_workspace": (_sz, [_i64, _i32, _i32, _i32, _int, _int]),
     "moe_grouped_ffn_fwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 11 + [_c_void_p, _sz, _c_void_p]),
-    "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 16 + [_c_void_p, _sz, _c_void_p]),
+    "moe_grouped_ffn_bwd": (_int, [_i64, _i32, _i32, _i32, _int] + [_c_void_p] * 18 + [_c_void_p, _sz, _c_void_p]),
     "moe_mx_act_bytes": (_sz, [_i64, _i32]),
+    "moe_mx_tok_rows": (_i64, [_i64, _i32]),
+    "moe_mx_tok_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_dispatch_mx_tok": (_int, [_c_void_p, _i64, _i32, _i32, _i32] + [_c_void_p] * 7),
+    "moe_combine_bwd_mx_tok": (_int, [_c_void_p] * 7 + [_i64, _i32, _i32, _i32] + [_c_void_p] * 5),
     "moe_dispatch_mx": (_int, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine_bwd_mx": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
                                   _c_void_p, _c_void_p, _c_void_p]),
@@ -202,6 +206,37 @@ def moe_dispatch_mx(x, perm_dst, k, out=None, mx=None):
     return out, mx
 
 
+def moe_mx_tok_buffer(rows, E, cols, device):
+    """Caller buffer for the token-axis MX layout: E4M3 codes [cols, moe_mx_tok_rows(rows, E)], then grouped scales."""
+    n = lib().moe_mx_tok_bytes(rows, E, cols)
+    if n == 0:
+        raise MoeError(f"moe_mx_tok_bytes({rows}, {E}, {cols}): unsupported size")
+    return _ws(n, device)
+
+
+def mx_tok_split(buf, rows, E, cols):
+    """(codes uint8 [cols, Rp], grouped scale bytes uint8 [Rp / 32 * cols]) views of a token-axis MX buffer."""
+    rp = lib().moe_mx_tok_rows(rows, E)
+    off = -(-rp * cols // 256) * 256
+    return buf[:rp * cols].view(cols, rp), buf[off:off + rp // 32 * cols]
+
+
+def moe_dispatch_mx_tok(x, route, k, E, out=None, mx=None, mxt=None, write_rows=False):
+    """Both MX layouts of the expert rows of x (rows and token-axis), from the routing `route` (perm_src,
+    offsets, mx_blk_offsets); the bf16 rows too when write_rows or `out` is given.  Returns (x_perm or None, mx,
+    mxt)."""
+    T, d = x.shape
+    R = T * k
+    if out is None and write_rows:
+        out = torch.empty((R, d), dtype=x.dtype, device=x.device)
+    mx = moe_mx_act_buffer(R, d, x.device) if mx is None else mx
+    mxt = moe_mx_tok_buffer(R, E, d, x.device) if mxt is None else mxt
+    _check(lib().moe_dispatch_mx_tok(_p(x), T, d, k, E, _p(route["perm_src"]), _p(route["offsets"]),
+                                     _p(route["mx_blk_offsets"]), _p(out), _p(mx), _p(mxt), _stream()),
+           "moe_dispatch_mx_tok")
+    return out, mx, mxt
+
+
 def moe_dispatch_bwd(dx_perm, perm_dst, k, out=None):
     R, d = dx_perm.shape
     T = R // k
@@ -242,6 +277,24 @@ def moe_combine_bwd_mx(dout, y_perm, gates, perm_dst, dy_perm=None, dgates=None,
     return dy_perm, dgates, mx
 
 
+def moe_combine_bwd_mx_tok(dout, y_perm, gates, route, E, dy_perm=None, dgates=None, mx=None, mxt=None,
+                           write_rows=False):
+    """dgates, and dY = gate x dout in both MX layouts (rows and token-axis); the bf16 rows too when write_rows
+    or `dy_perm` is given.  Returns (dy_perm or None, dgates, mx, mxt)."""
+    T, k = gates.shape
+    d = dout.shape[1]
+    R = T * k
+    if dy_perm is None and write_rows:
+        dy_perm = torch.empty_like(y_perm)
+    dgates = torch.empty((T, k), dtype=torch.float32, device=dout.device) if dgates is None else dgates
+    mx = moe_mx_act_buffer(R, d, dout.device) if mx is None else mx
+    mxt = moe_mx_tok_buffer(R, E, d, dout.device) if mxt is None else mxt
+    _check(lib().moe_combine_bwd_mx_tok(_p(dout), _p(y_perm), _p(gates), _p(route["perm_dst"]), _p(route["perm_src"]),
+                                        _p(route["offsets"]), _p(route["mx_blk_offsets"]), T, d, k, E, _p(dy_perm),
+                                        _p(dgates), _p(mx), _p(mxt), _stream()), "moe_combine_bwd_mx_tok")
+    return dy_perm, dgates, mx, mxt
+
+
 def moe_route_stats(counts, out=None):
     """counts [E] int32 (device) -> int32 [4] on the device: max rows, min rows, empty experts, total rows."""
     E = counts.shape[0]
@@ -256,13 +309,15 @@ def moe_grouped_ffn_workspace(R, E, d, f, prec, is_bwd):
     return lib().moe_grouped_ffn_workspace(R, E, d, f, _PREC[prec], int(is_bwd))
 
 
-def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, ws=None, mx_wcache=None, x_mx=None):
-    R, d = x_perm.shape
-    E, _, f = w_gate.shape
-    dev = x_perm.device
+def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, ws=None, mx_wcache=None, x_mx=None,
+                        rows=None):
+    """x_perm may be None with prec "mxfp8" and x_mx given; then `rows` (R) is required."""
+    E, d, f = w_gate.shape
+    R = x_perm.shape[0] if x_perm is not None else int(rows)
+    dev = w_gate.device
     if out is None:
-        out = {name: torch.empty((R, f), dtype=x_perm.dtype, device=dev) for name in ("h_gate", "h_up", "a_act")}
-        out["y_perm"] = torch.empty((R, d), dtype=x_perm.dtype, device=dev)
+        out = {name: torch.empty((R, f), dtype=w_gate.dtype, device=dev) for name in ("h_gate", "h_up", "a_act")}
+        out["y_perm"] = torch.empty((R, d), dtype=w_gate.dtype, device=dev)
     ws = _ws(moe_grouped_ffn_workspace(R, E, d, f, prec, 0), dev) if ws is None else ws
     _check(lib().moe_grouped_ffn_fwd(R, E, d, f, _PREC[prec], _p(offsets), _p(x_perm), _p(w_gate), _p(w_up),
                                      _p(w_down), _p(mx_wcache), _p(x_mx), _p(out["h_gate"]), _p(out["h_up"]),
@@ -272,17 +327,19 @@ def moe_grouped_ffn_fwd(x_perm, offsets, w_gate, w_up, w_down, prec, out=None, w
 
 
 def moe_grouped_ffn_bwd(dy_perm, x_perm, h_gate, h_up, a_act, offsets, mx_blk_offsets, w_gate, w_up, w_down, prec,
-                        out=None, ws=None, mx_wcache=None, dy_mx=None):
-    R, d = x_perm.shape
-    E, _, f = w_gate.shape
-    dev = x_perm.device
+                        out=None, ws=None, mx_wcache=None, dy_mx=None, x_mxt=None, dy_mxt=None):
+    """With prec "mxfp8", x_perm may be None when x_mxt is given, dy_perm when dy_mx and dy_mxt are."""
+    E, d, f = w_gate.shape
+    R = h_gate.shape[0]
+    dev = h_gate.device
     if out is None:
-        out = {"dx_perm": torch.empty_like(x_perm), "dw_gate": torch.empty_like(w_gate),
+        out = {"dx_perm": torch.empty((R, d), dtype=h_gate.dtype, device=dev), "dw_gate": torch.empty_like(w_gate),
                "dw_up": torch.empty_like(w_up), "dw_down": torch.empty_like(w_down)}
     ws = _ws(moe_grouped_ffn_workspace(R, E, d, f, prec, 1), dev) if ws is None else ws
     _check(lib().moe_grouped_ffn_bwd(R, E, d, f, _PREC[prec], _p(offsets), _p(mx_blk_offsets), _p(dy_perm),
                                      _p(x_perm), _p(h_gate), _p(h_up), _p(a_act), _p(w_gate), _p(w_up), _p(w_down),
-                                     _p(mx_wcache), _p(dy_mx), _p(out["dx_perm"]), _p(out["dw_gate"]), _p(out["dw_up"]),
+                                     _p(mx_wcache), _p(dy_mx), _p(x_mxt), _p(dy_mxt), _p(out["dx_perm"]),
+                                     _p(out["dw_gate"]), _p(out["dw_up"]),
                                      _p(out["dw_down"]), _p(ws), ws.numel(), _stream()), "moe_grouped_ffn_bwd")
     return out
 

@@ -161,7 +161,7 @@ void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t m
 
 using namespace moe;
 
-extern "C" int moe_abi_version(void) { return 3; }
+extern "C" int moe_abi_version(void) { return 4; }
 
 extern "C" const char* moe_status_str(int status) {
   switch (status) {
@@ -205,7 +205,8 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   if (!shape_ok(sh)) return MOE_EINVAL;
   if (!shape_supported(sh)) return MOE_EUNSUPPORTED;
   if (!offsets || !w_gate || !w_up || !w_down || !ws) return MOE_EINVAL;
-  if (R > 0 && (!x_perm || !h_gate || !h_up || !a_act || !y_perm)) return MOE_EINVAL;
+  if (R > 0 && ((!x_perm && !(x_mx && prec == MOE_MXFP8)) || !h_gate || !h_up || !a_act || !y_perm))
+    return MOE_EINVAL;
   for (const void* p : {x_perm, w_gate, w_up, w_down, mx_wcache, x_mx, (const void*)h_gate, (const void*)h_up,
                         (const void*)a_act, (const void*)y_perm, (const void*)ws})
     if (p && !aligned16(p)) return MOE_EINVAL;
@@ -239,19 +240,23 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
                                    const int32_t* mx_blk_offsets, const void* dy_perm, const void* x_perm,
                                    const void* h_gate, const void* h_up, const void* a_act, const void* w_gate,
                                    const void* w_up, const void* w_down, const void* mx_wcache, const void* dy_mx,
-                                   void* dx_perm, void* dw_gate, void* dw_up, void* dw_down, void* ws,
-                                   size_t ws_bytes, void* stream) {
+                                   const void* x_mxt, const void* dy_mxt, void* dx_perm, void* dw_gate,
+                                   void* dw_up, void* dw_down, void* ws, size_t ws_bytes, void* stream) {
   const FfnShape sh{R, E, d, f, prec};
   if (!shape_ok(sh)) return MOE_EINVAL;
   if (!shape_supported(sh)) return MOE_EUNSUPPORTED;
   if (!offsets || !w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down || !ws) return MOE_EINVAL;
-  if (R > 0 && (!dy_perm || !x_perm || !h_gate || !h_up || !a_act || !dx_perm)) return MOE_EINVAL;
+  if ((dy_mx || x_mxt || dy_mxt) && prec != MOE_MXFP8) return MOE_EINVAL;
+  // x_perm is read only for its token-axis MX layout, dy_perm only for its two MX layouts (MOE_MXFP8)
+  const bool need_x = prec != MOE_MXFP8 || !x_mxt;
+  const bool need_dy = prec != MOE_MXFP8 || !dy_mx || !dy_mxt;
+  if (R > 0 && ((need_dy && !dy_perm) || (need_x && !x_perm) || !h_gate || !h_up || !a_act || !dx_perm))
+    return MOE_EINVAL;
   if (prec == MOE_MXFP8 && !mx_blk_offsets) return MOE_EINVAL;
-  for (const void* p : {dy_perm, x_perm, h_gate, h_up, a_act, w_gate, w_up, w_down, mx_wcache, dy_mx,
+  for (const void* p : {dy_perm, x_perm, h_gate, h_up, a_act, w_gate, w_up, w_down, mx_wcache, dy_mx, x_mxt, dy_mxt,
                         (const void*)dx_perm, (const void*)dw_gate, (const void*)dw_up, (const void*)dw_down,
                         (const void*)ws})
     if (p && !aligned16(p)) return MOE_EINVAL;
-  if (dy_mx && prec != MOE_MXFP8) return MOE_EINVAL;
   if (ws_bytes < ffn_ws_bytes(sh, 1)) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bm = tile_bm(prec, R, E);
@@ -279,7 +284,7 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   if (prec == MOE_MXFP8) {
     char* mxs = wsb + tb + 2 * hbytes;
     return mx_ffn_bwd(a, mt, mx_blk_offsets, static_cast<const char*>(mx_wcache), static_cast<const uint8_t*>(dy_mx),
-                      mxs, s);
+                      static_cast<const uint8_t*>(x_mxt), static_cast<const uint8_t*>(dy_mxt), mxs, s);
   }
   auto launch = prec == MOE_F32 ? launch_ffn_f32 : launch_ffn_bf16;
   int st = MOE_OK;

@@ -740,10 +740,7 @@ QPair take_q(Carve& c, int64_t elems) {
   return r;
 }
 
-// token-axis length: every expert segment padded to 32 tokens, the total to a
-// whole number of scale groups (128 tokens) plus one zero group, so that a
-// K-step starting mid-group never reads a group past the end
-int64_t token_pad(int64_t R, int E) { return 128 * (cdiv(cdiv(R, 32) + E, 4) + 1); }
+int64_t token_pad(int64_t R, int E) { return mx_token_rows(R, E); }
 
 // Lay out (or size, when base is null) the forward and backward scratch areas.
 struct FwdBufs {
@@ -861,7 +858,7 @@ int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, const ui
 }
 
 int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache,
-               const uint8_t* dy_mx, char* scratch, hipStream_t s) {
+               const uint8_t* dy_mx, const uint8_t* x_mxt, const uint8_t* dy_mxt, char* scratch, hipStream_t s) {
   Carve c{scratch};
   const BwdBufs b = carve_bwd(c, a.R, a.E, a.d, a.f);
   const int bf = MOE_BF16;
@@ -900,13 +897,17 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
     if (st != MOE_OK) return st;
     // weight gradients: every operand along tokens, per expert segment, transposed
     launch_mx_cols(a.act, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.at.q, b.at.s, s, true, mx_blk_offsets);
-    launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s, true, mx_blk_offsets);
-    launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s, true, mx_blk_offsets);
+    if (!dy_mxt) launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s, true, mx_blk_offsets);
+    if (!x_mxt) launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s, true, mx_blk_offsets);
     launch_mx_cols(a.dhg, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhgt.q, b.dhgt.s, s, true, mx_blk_offsets);
     launch_mx_cols(a.dhu, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhut.q, b.dhut.s, s, true, mx_blk_offsets);
   }
-  m.atq = b.at.q; m.ats = b.at.s; m.dytq = b.dyt.q; m.dyts = b.dyt.s;
-  m.xtq = b.xt.q; m.xts = b.xt.s;
+  const size_t tcodes = align_up(static_cast<size_t>(a.d) * rp, 256);  // token-axis codes of a d-wide operand
+  m.atq = b.at.q; m.ats = b.at.s;
+  m.dytq = dy_mxt ? dy_mxt : b.dyt.q;
+  m.dyts = dy_mxt ? dy_mxt + tcodes : b.dyt.s;
+  m.xtq = x_mxt ? x_mxt : b.xt.q;
+  m.xts = x_mxt ? x_mxt + tcodes : b.xt.s;
   m.dhgtq = b.dhgt.q; m.dhgts = b.dhgt.s; m.dhutq = b.dhut.q; m.dhuts = b.dhut.s;
   st = launch_mx_kind(kG4, m, max_tiles, s);
   if (st == MOE_OK) st = launch_mx_kind(kG6, m, max_tiles, s);

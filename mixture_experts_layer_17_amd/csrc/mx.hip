@@ -298,6 +298,192 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
   }
 }
 
+// Destination-major gather of an expert-major buffer's rows into both MX
+// layouts at once (launch_mx_gather): a workgroup takes 4 consecutive 32-row
+// blocks of the padded token axis (in block order, each block inside one expert
+// segment) and NSUB consecutive 64-column subtiles of them.  Each tile row names
+// its expert row and, through the routing's permutation, the token row it
+// copies (times the slot's gate for dY, rounded to bf16 as the combine backward
+// stores it); a subtile's loads are issued before the one before it is
+// encoded, so the scattered row reads stay in flight.  A subtile is quantised
+// down the tokens exactly as mx_cols_kernel does with segments, and along d
+// into the rows layout as mx_cols_kernel's BOTH pass does (the workgroup writes
+// whole 128-byte lines of it); padding rows are zero in the token layout and
+// absent from the rows layout.
+template <bool SCALED, int NSUB>
+__global__ __launch_bounds__(256) void mx_gather_kernel(const uint16_t* __restrict__ src, int64_t R, int d, int k,
+                                                       const int32_t* __restrict__ perm_src,
+                                                       const float* __restrict__ gates,
+                                                       const int32_t* __restrict__ seg, const int32_t* __restrict__ blk,
+                                                       int nseg, int64_t ldq, uint16_t* __restrict__ rows_out,
+                                                       uint8_t* __restrict__ qr, uint8_t* __restrict__ scr,
+                                                       uint8_t* __restrict__ qt, uint8_t* __restrict__ sct) {
+  constexpr int VEC = 8;               // bf16 elements per 16-byte vector
+  constexpr int VPR = kColW / VEC;     // vectors per tile row
+  constexpr int LDT = kColW + VEC;     // padded tile row
+  constexpr int NV = 128 * VPR / 256;  // vectors per thread and subtile
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * LDT];
+  __shared__ uint32_t obuf[kColW][33];
+  __shared__ uint8_t osc[kColW][4];
+  __shared__ int32_t s_off[kMaxE + 1];
+  __shared__ int32_t s_blk[kMaxE + 1];
+  __shared__ int64_t s_src[128];  // element offset of the tile row's token row in src; -1: padding
+  __shared__ int64_t s_row[128];  // the tile row's expert row; -1: padding
+  __shared__ float s_gate[128];
+  __shared__ int64_t b_r0[4];
+  __shared__ int b_nv[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t gx = d / (kColW * NSUB), gy = ldq / 128;  // d % (64 NSUB) == 0, ldq % 128 == 0
+  const int64_t bx = blockIdx.x % gx, by = blockIdx.x / gx;
+  if (by >= gy) return;
+  const int64_t nblk = ldq / 32;
+  const int64_t b0 = by * 4;
+  for (int i = tid; i <= nseg; i += blockDim.x) {
+    s_off[i] = seg[i];
+    s_blk[i] = blk[i];
+  }
+  __syncthreads();
+  if (tid < 4) {
+    const int64_t b = b0 + tid;
+    int64_t r0 = 0, nv = 0;
+    if (b < nblk && b < s_blk[nseg]) {  // blocks past the last segment stay zero padding
+      int lo = 0, hi = nseg;            // s with s_blk[s] <= b < s_blk[s+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_blk[mid] <= b) lo = mid; else hi = mid;
+      }
+      r0 = s_off[lo] + (b - s_blk[lo]) * 32;
+      const int64_t end = s_off[lo + 1] < R ? s_off[lo + 1] : R;
+      nv = end - r0;
+      if (nv > 32) nv = 32;
+      if (nv < 0) nv = 0;
+    }
+    b_r0[tid] = r0;
+    b_nv[tid] = static_cast<int>(nv);
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int bi = tid >> 5, r = tid & 31;
+    int64_t row = -1, off = -1;
+    float g = 0.f;
+    if (r < b_nv[bi]) {
+      row = b_r0[bi] + r;
+      const int32_t slot = perm_src[row];
+      off = static_cast<int64_t>(slot / k) * d;
+      if constexpr (SCALED) g = gates[slot];
+    }
+    s_row[tid] = row;
+    s_src[tid] = off;
+    s_gate[tid] = g;
+  }
+  __syncthreads();
+  // vector i of this thread: tile row (tid + 256 i) / VPR, 16-byte column (tid + 256 i) % VPR
+  auto load = [&](int64_t c0, uint4 (&out)[NV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + 256 * i;
+      const int tr = v / VPR, cv = v - tr * VPR;
+      const int64_t off = s_src[tr];
+      out[i] = off >= 0 ? *reinterpret_cast<const uint4*>(src + off + c0 + cv * VEC) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 nxt[NV];
+  load(bx * NSUB * kColW, nxt);
+#pragma unroll 1
+  for (int sub = 0; sub < NSUB; ++sub) {
+    const int64_t c0 = (bx * NSUB + sub) * kColW;
+    uint4 cur[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+    if (sub + 1 < NSUB) load(c0 + kColW, nxt);
+    __syncthreads();  // the previous subtile's reads of the tile and of obuf are done
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + 256 * i;
+      const int tr = v / VPR, cv = v - tr * VPR;
+      uint4 val = cur[i];
+      if (s_src[tr] >= 0) {
+        if constexpr (SCALED) {
+          float f[VEC];
+          Elem<uint16_t>::unpack(val, f);
+          const float g = s_gate[tr];
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) f[j] = g * f[j];
+          val = Elem<uint16_t>::pack(f);
+        }
+        if (rows_out) *reinterpret_cast<uint4*>(rows_out + s_row[tr] * d + c0 + cv * VEC) = val;
+      }
+      *reinterpret_cast<uint4*>(tile + tr * LDT + cv * VEC) = val;
+    }
+    __syncthreads();
+    {
+      // down the tokens: wave w encodes block w, one column per lane
+      float v[32];
+      float amax = 0.f;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        v[r] = Elem<uint16_t>::load1(tile, (wave * 32 + r) * LDT + lane);
+        amax = fmaxf(amax, fabsf(v[r]));
+      }
+      const int e = mx_block_exponent(amax);
+      const float inv = mx_inv_scale(e);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        obuf[lane][wave * 8 + q] =
+            e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
+      osc[lane][wave] = static_cast<uint8_t>(e + 127);
+    }
+    __syncthreads();
+    for (int c = tid; c < kColW * 8; c += blockDim.x) {
+      const int oc = c >> 3, ch = c & 7;  // 16-byte chunk ch of output row oc (block ch / 2)
+      if (b0 + (ch >> 1) < nblk) {
+        const uint32_t* o = &obuf[oc][ch * 4];
+        *reinterpret_cast<uint4*>(qt + (c0 + oc) * ldq + b0 * 32 + ch * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    if (tid < kColW) {
+      // the four blocks of this workgroup are one group: 64 consecutive scale words
+      const uint32_t w =
+          osc[tid][0] | (osc[tid][1] << 8) | (osc[tid][2] << 16) | (static_cast<uint32_t>(osc[tid][3]) << 24);
+      reinterpret_cast<uint32_t*>(sct)[(b0 >> 2) * d + c0 + tid] = w;
+    }
+    // along d: four lanes per tile row (16 columns each, two lanes per 32-element block)
+    const int qq = tid & 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tr = h * 64 + (tid >> 2);
+      const int64_t row = s_row[tr];
+      float v[16];
+      const uint16_t* tp = tile + tr * LDT + qq * 16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float tmp[VEC];
+        Elem<uint16_t>::unpack(*reinterpret_cast<const uint4*>(tp + u * VEC), tmp);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) v[u * VEC + j] = tmp[j];
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      const int e = mx_block_exponent(amax);
+      const float inv = mx_inv_scale(e);
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
+      // the row's two scale bytes (blocks c0/32 and c0/32 + 1, one half of its group word) from lanes qq = 0, 2
+      const uint32_t pair =
+          static_cast<uint32_t>(e + 127) | (static_cast<uint32_t>(__shfl_xor(e, 2, 64) + 127) << 8);
+      if (row >= 0) {
+        *reinterpret_cast<uint4*>(qr + row * d + c0 + qq * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (qq == 0)
+          *reinterpret_cast<uint16_t*>(scr + scale_index(true, row, c0 / 32, R, d / 32)) = static_cast<uint16_t>(pair);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 void launch_mx_rows(const void* src, int src_dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sc,
@@ -362,6 +548,24 @@ void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows,
   else
     MOE_LAUNCH("mx_quantize_both", (mx_cols_kernel<uint16_t, true, true>), grid, dim3(256), 0, s,
                static_cast<const uint16_t*>(src), batch, rows, cols, nullptr, nullptr, 0, rows, qc, sc, qr, scr);
+}
+
+void launch_mx_gather(const uint16_t* src, int64_t R, int d, int k, const int32_t* perm_src, const float* gates,
+                      const int32_t* seg, const int32_t* blk, int nseg, uint16_t* rows_out, uint8_t* qr,
+                      uint8_t* scr, uint8_t* qt, uint8_t* sct, hipStream_t s) {
+  if (R == 0 || d == 0) return;
+  const int64_t ldq = mx_token_rows(R, nseg);
+  const bool four = d % (4 * kColW) == 0;  // four 64-column subtiles per workgroup, else two (d % 128 == 0)
+  const dim3 grid(static_cast<unsigned>((d / (kColW * (four ? 4 : 2))) * (ldq / 128)));
+#define MOE_GATHER(SC, NS)                                                                                         \
+  MOE_LAUNCH("mx_gather", (mx_gather_kernel<SC, NS>), grid, dim3(256), 0, s, src, R, d, k, perm_src, gates, seg, \
+             blk, nseg, ldq, rows_out, qr, scr, qt, sct)
+  if (gates) {
+    if (four) MOE_GATHER(true, 4); else MOE_GATHER(true, 2);
+  } else {
+    if (four) MOE_GATHER(false, 4); else MOE_GATHER(false, 2);
+  }
+#undef MOE_GATHER
 }
 
 }  // namespace moe

@@ -67,16 +67,34 @@ void launch_mx_cols(const void* src, int src_dtype, int64_t batch, int64_t rows,
 void launch_mx_both(const void* src, int src_dtype, int64_t batch, int64_t rows, int64_t cols, uint8_t* qc,
                     uint8_t* sc, uint8_t* qr, uint8_t* scr, hipStream_t s);
 
+// Token-axis length of the weight gradients' MX operands: every expert segment
+// padded to 32 tokens, the total to a whole number of scale groups (128
+// tokens) plus one zero group, so that a K-step starting mid-group never reads
+// a group past the end.
+inline int64_t mx_token_rows(int64_t R, int E) { return 128 * (cdiv(cdiv(R, 32) + E, 4) + 1); }
+
+//  destination-major gather of an expert-major buffer's rows into both of its MX layouts: the rows layout
+//  (codes qr [R, d], scales grouped over the R rows: word of (row, group G) at scr + 4 (G R + row)) and the
+//  token-axis layout (as launch_mx_cols with segments and grouped scales: qt [d][ldq], ldq = mx_token_rows).
+//  Expert row r holds source row perm_src[r] / k of src [T, d] (bf16), times gates[perm_src[r]] rounded to
+//  bf16 when gates is not NULL; rows_out [R, d] (bf16, may be NULL) receives the rows themselves.
+//  seg: nseg + 1 segment offsets, blk: their 32-row block-count prefix (device).  d % 128 == 0.
+void launch_mx_gather(const uint16_t* src, int64_t R, int d, int k, const int32_t* perm_src, const float* gates,
+                      const int32_t* seg, const int32_t* blk, int nseg, uint16_t* rows_out, uint8_t* qr,
+                      uint8_t* scr, uint8_t* qt, uint8_t* sct, hipStream_t s);
+
 // MXFP8 expert FFN (gemm_mx.hip).
 size_t mx_ffn_scratch_bytes(int64_t R, int E, int d, int f, int is_bwd);
 int ffn_mx_bm(int64_t R, int E);  // row-tile height for this workload
 //  wcache: NULL, or a weight cache built by mx_wcache_build for the same weights (then no weight is quantised).
 //  x_mx / dy_mx: NULL, or X / dY already in the MX rows layout (codes [R, d], then at the next 256-byte boundary
-//  the grouped scale words), as moe_dispatch_mx / moe_combine_bwd_mx write them.
+//  the grouped scale words), as moe_dispatch_mx / moe_combine_bwd_mx write them.  x_mxt / dy_mxt: NULL, or X /
+//  dY already in the token-axis layout (codes [d][mx_token_rows(R, E)], then at the next 256-byte boundary the
+//  grouped scale words), as moe_dispatch_mx_tok / moe_combine_bwd_mx_tok write them.
 int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, const uint8_t* x_mx, char* scratch,
                hipStream_t s);
 int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offsets, const char* wcache,
-               const uint8_t* dy_mx, char* scratch, hipStream_t s);
+               const uint8_t* dy_mx, const uint8_t* x_mxt, const uint8_t* dy_mxt, char* scratch, hipStream_t s);
 size_t mx_wcache_bytes(int E, int d, int f);
 void mx_wcache_build(const void* wg, const void* wu, const void* wd, int E, int d, int f, char* cache,
                      hipStream_t s);

@@ -105,7 +105,9 @@ __global__ __launch_bounds__(64 * kWaves) void gather_sum_kernel(const T* __rest
   }
 }
 
-template <typename T, int KP>
+// With WRITE_DY false only dgates is computed (dY goes to its MX layouts
+// through mx_gather_kernel instead).
+template <typename T, int KP, bool WRITE_DY = true>
 __global__ __launch_bounds__(64 * kWaves) void combine_bwd_kernel(const T* __restrict__ dout,
                                                                  const T* __restrict__ y_perm, int64_t Tn, int d,
                                                                  int k, const int32_t* __restrict__ perm_dst,
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(64 * kWaves) void combine_bwd_kernel(const T* __res
 #pragma unroll
           for (int i = 0; i < V; ++i) { p += o[i] * y[i]; sv[i] = g[j] * o[i]; }
           dot[j] += p;
-          reinterpret_cast<uint4*>(dy_perm + rows[j])[c] = Elem<T>::pack(sv);
+          if constexpr (WRITE_DY) reinterpret_cast<uint4*>(dy_perm + rows[j])[c] = Elem<T>::pack(sv);
         }
       }
     }
@@ -338,15 +340,15 @@ int launch_gather_sum(const char* name, const T* src, int64_t Tn, int d, int k, 
   return launch_status();
 }
 
-template <typename T>
+template <typename T, bool WRITE_DY = true>
 int launch_combine_bwd(const T* dout, const T* y_perm, int64_t Tn, int d, int k, const int32_t* perm_dst,
                        const float* gates, T* dy_perm, float* dgates, hipStream_t s) {
   if (k <= 4)
-    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, 4>), grid_for(Tn), dim3(64 * kWaves), 0, s, dout, y_perm, Tn, d,
-               k, perm_dst, gates, dy_perm, dgates);
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, 4, WRITE_DY>), grid_for(Tn), dim3(64 * kWaves), 0, s, dout,
+               y_perm, Tn, d, k, perm_dst, gates, dy_perm, dgates);
   else
-    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, kMaxK>), grid_for(Tn), dim3(64 * kWaves), 0, s, dout, y_perm,
-               Tn, d, k, perm_dst, gates, dy_perm, dgates);
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, kMaxK, WRITE_DY>), grid_for(Tn), dim3(64 * kWaves), 0, s, dout,
+               y_perm, Tn, d, k, perm_dst, gates, dy_perm, dgates);
   return launch_status();
 }
 
@@ -413,6 +415,68 @@ extern "C" int moe_combine_bwd_mx(const void* dout, const void* y_perm, const fl
   else
     MOE_LAUNCH("combine_bwd", combine_bwd_mx_kernel<kMaxK>, grid_for(T), dim3(64 * kWaves), 0, s, dout16, y16, T, d,
                k, perm_dst, gates, dy16, dgates, q, sw);
+  return launch_status();
+}
+
+extern "C" int64_t moe_mx_tok_rows(int64_t R, int32_t E) {
+  if (R < 0 || E < 1 || E > kMaxE) return 0;
+  return mx_token_rows(R, E);
+}
+
+extern "C" size_t moe_mx_tok_bytes(int64_t R, int32_t E, int32_t cols) {
+  if (R < 0 || E < 1 || E > kMaxE || cols <= 0 || cols % 128) return 0;
+  const int64_t rp = mx_token_rows(R, E);
+  return align_up(static_cast<size_t>(rp) * cols, 256) + static_cast<size_t>(rp / 32) * cols;
+}
+
+namespace {
+// Shared checks of the two token-axis calls; R = T k.
+int tok_args_ok(int64_t T, int32_t d, int32_t k, int32_t E, const int32_t* perm_src, const int32_t* offsets,
+                const int32_t* mx_blk_offsets, const void* rows_out, const void* mx, const void* mxt) {
+  if (!dims_ok(MOE_BF16, T, d, k) || E < 1 || E > kMaxE) return MOE_EINVAL;
+  if (d % 128) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!perm_src || !offsets || !mx_blk_offsets || !mx || !mxt || !aligned16(mx) || !aligned16(mxt) ||
+      (rows_out && !aligned16(rows_out)))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_dispatch_mx_tok(const void* x, int64_t T, int32_t d, int32_t k, int32_t E, const int32_t* perm_src,
+                                   const int32_t* offsets, const int32_t* mx_blk_offsets, void* x_perm, void* x_mx,
+                                   void* x_mxt, void* stream) {
+  const int st = tok_args_ok(T, d, k, E, perm_src, offsets, mx_blk_offsets, x_perm, x_mx, x_mxt);
+  if (st != MOE_OK || T == 0) return st;
+  if (!x || !aligned16(x)) return MOE_EINVAL;
+  const int64_t R = T * k;
+  uint8_t* q = static_cast<uint8_t*>(x_mx);
+  uint8_t* qt = static_cast<uint8_t*>(x_mxt);
+  launch_mx_gather(static_cast<const uint16_t*>(x), R, d, k, perm_src, nullptr, offsets, mx_blk_offsets, E,
+                   static_cast<uint16_t*>(x_perm), q, q + align_up(static_cast<size_t>(R) * d, 256), qt,
+                   qt + align_up(static_cast<size_t>(mx_token_rows(R, E)) * d, 256), static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+extern "C" int moe_combine_bwd_mx_tok(const void* dout, const void* y_perm, const float* gates,
+                                      const int32_t* perm_dst, const int32_t* perm_src, const int32_t* offsets,
+                                      const int32_t* mx_blk_offsets, int64_t T, int32_t d, int32_t k, int32_t E,
+                                      void* dy_perm, float* dgates, void* dy_mx, void* dy_mxt, void* stream) {
+  const int st = tok_args_ok(T, d, k, E, perm_src, offsets, mx_blk_offsets, dy_perm, dy_mx, dy_mxt);
+  if (st != MOE_OK || T == 0) return st;
+  if (!dout || !y_perm || !gates || !perm_dst || !dgates || !aligned16(dout) || !aligned16(y_perm)) return MOE_EINVAL;
+  const int64_t R = T * k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* dout16 = static_cast<const uint16_t*>(dout);
+  // dgates (token-major: each token's k dot products), then dY = gate x dout into both MX layouts
+  const int r = launch_combine_bwd<uint16_t, false>(dout16, static_cast<const uint16_t*>(y_perm), T, d, k, perm_dst,
+                                                    gates, nullptr, dgates, s);
+  if (r != MOE_OK) return r;
+  uint8_t* q = static_cast<uint8_t*>(dy_mx);
+  uint8_t* qt = static_cast<uint8_t*>(dy_mxt);
+  launch_mx_gather(dout16, R, d, k, perm_src, gates, offsets, mx_blk_offsets, E, static_cast<uint16_t*>(dy_perm), q,
+                   q + align_up(static_cast<size_t>(R) * d, 256), qt,
+                   qt + align_up(static_cast<size_t>(mx_token_rows(R, E)) * d, 256), s);
   return launch_status();
 }
 

@@ -62,14 +62,17 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu_step(w: wl.Workload, inp: dict, mx_weight_cache: bool = False, mx_weights_per_step: bool = False,
-                 mx_fused_movement: bool = True) -> tuple[dict, L.LayerStep]:
+                 mx_movement: str = "tok", keep_rows: bool = True) -> tuple[dict, L.LayerStep]:
+    """One layer step; the MXFP8 movement as the layer's default, the bf16 expert rows kept (keep_rows) so that
+    the dispatch's rows are checked too."""
     step = L.LayerStep(w, L.to_device(inp), mx_weight_cache=mx_weight_cache, mx_weights_per_step=mx_weights_per_step,
-                       mx_fused_movement=mx_fused_movement)
+                       mx_movement=mx_movement, keep_rows=keep_rows)
     step.step()
     torch.cuda.synchronize()
     res = {k: host(v) for k, v in step.route.items()}
     res["logits"] = host(step.logits)
-    res["x_perm"] = host(step.x_perm)
+    if step.x_perm is not None:
+        res["x_perm"] = host(step.x_perm)
     res.update({k: host(v) for k, v in step.ffn.items()})
     res["out"] = host(step.out)
     res["dgates"] = host(step.dgates)

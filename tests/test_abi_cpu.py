@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert L.moe_status_str(0) == b"ok"
     assert L.moe_status_str(3) == b"workspace too small"
 
@@ -68,10 +68,12 @@ def test_ffn_validation(L):
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1000, 1, *args, FAKE, 1 << 30, s) == EUNSUP   # f % 64
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 7, *args, FAKE, 1 << 30, s) == EINVAL   # bad precision
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *no_xmx, FAKE, 16, s) == EWS
-    bargs = [FAKE] * 16
-    no_dymx = [FAKE] * 11 + [None] + [FAKE] * 4  # dy_mx NULL
+    # backward pointers: offsets, mx_blk_offsets, dy_perm, x_perm, h_gate, h_up, a_act, w_gate, w_up, w_down,
+    # mx_wcache, dy_mx, x_mxt, dy_mxt, dx_perm, dw_gate, dw_up, dw_down
+    bargs = [FAKE] * 18
+    no_dymx = [FAKE] * 11 + [None] * 3 + [FAKE] * 4  # dy_mx, x_mxt, dy_mxt NULL
     assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *no_dymx, FAKE, 16, s) == EWS
-    bargs_nomx = [FAKE, None] + [FAKE] * 14
+    bargs_nomx = [FAKE, None] + [FAKE] * 16
     assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 2, *bargs_nomx, FAKE, 1 << 40, s) == EINVAL
     unaligned = [FAKE] + [ctypes.c_void_p(0x10008)] + [FAKE] * 4 + [None] + [FAKE] * 4
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *unaligned, FAKE, 1 << 30, s) == EINVAL
@@ -80,6 +82,23 @@ def test_ffn_validation(L):
     # pre-quantised activations: MXFP8 only
     assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 1, *args, FAKE, 1 << 40, s) == EINVAL   # x_mx with bf16
     assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *bargs, FAKE, 1 << 40, s) == EINVAL  # dy_mx with bf16
+    for i in (12, 13):                                                                       # x_mxt, dy_mxt with bf16
+        only = no_dymx.copy()
+        only[i] = FAKE
+        assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 1, *only, FAKE, 1 << 40, s) == EINVAL
+    # MXFP8: x_perm / dy_perm may be NULL when their MX layouts are given (validation passes: the tiny
+    # workspace is what is refused), not otherwise
+    no_rows = bargs.copy()
+    no_rows[2] = no_rows[3] = None
+    assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 2, *no_rows, FAKE, 16, s) == EWS
+    for i in (11, 12, 13):
+        missing = no_rows.copy()
+        missing[i] = None
+        assert L.moe_grouped_ffn_bwd(1024, 8, 2048, 1024, 2, *missing, FAKE, 1 << 40, s) == EINVAL
+    fwd_no_x = [FAKE, None] + [FAKE] * 9
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 2, *fwd_no_x, FAKE, 16, s) == EWS
+    fwd_no_x[6] = None                                                                        # and no x_mx
+    assert L.moe_grouped_ffn_fwd(1024, 8, 2048, 1024, 2, *fwd_no_x, FAKE, 1 << 40, s) == EINVAL
 
 
 def test_mx_data_movement_validation(L):
@@ -92,6 +111,27 @@ def test_mx_data_movement_validation(L):
     assert L.moe_dispatch_mx(FAKE, 0, 256, 2, None, None, None, s) == 0                    # nothing to do
     assert L.moe_combine_bwd_mx(FAKE, FAKE, FAKE, FAKE, 10, 192, 2, FAKE, FAKE, FAKE, s) == EUNSUP
     assert L.moe_combine_bwd_mx(FAKE, FAKE, FAKE, FAKE, 10, 256, 2, FAKE, FAKE, ctypes.c_void_p(0x10004), s) == EINVAL
+    # token-axis layout: 32-row blocks per expert segment, padded to whole 128-token groups plus one
+    rp = 128 * (-(-(-(-1000 // 32) + 8) // 4) + 1)
+    assert L.moe_mx_tok_rows(1000, 8) == rp == 1408
+    assert L.moe_mx_tok_bytes(1000, 8, 256) == -(-rp * 256 // 256) * 256 + rp // 32 * 256
+    assert L.moe_mx_tok_bytes(1000, 8, 200) == 0 and L.moe_mx_tok_bytes(1000, 0, 256) == 0
+    assert L.moe_mx_tok_bytes(1000, 257, 256) == 0 and L.moe_mx_tok_rows(-1, 8) == 0
+    tok = [FAKE] * 3 + [None, FAKE, FAKE]        # perm_src, offsets, mx_blk_offsets, x_perm (none), x_mx, x_mxt
+    assert L.moe_dispatch_mx_tok(FAKE, 10, 200, 2, 8, *tok, s) == EUNSUP              # d % 128
+    assert L.moe_dispatch_mx_tok(FAKE, 10, 256, 2, 0, *tok, s) == EINVAL              # E < 1
+    assert L.moe_dispatch_mx_tok(FAKE, 10, 256, 2, 300, *tok, s) == EINVAL            # E > 256
+    assert L.moe_dispatch_mx_tok(FAKE, 10, 256, 2, 8, *tok[:5], None, s) == EINVAL    # null token-axis buffer
+    assert L.moe_dispatch_mx_tok(FAKE, 10, 256, 2, 8, FAKE, None, *tok[2:], s) == EINVAL  # null offsets
+    assert L.moe_dispatch_mx_tok(None, 10, 256, 2, 8, *tok, s) == EINVAL              # null x
+    assert L.moe_dispatch_mx_tok(FAKE, 10, 256, 2, 8, *tok[:3], ctypes.c_void_p(0x10004), *tok[4:], s) == EINVAL
+    assert L.moe_dispatch_mx_tok(None, 0, 256, 2, 8, *[None] * 6, s) == 0             # nothing to do
+    cb = [FAKE] * 7                               # dout, y_perm, gates, perm_dst, perm_src, offsets, mx_blk_offsets
+    out = [None, FAKE, FAKE, FAKE]                # dy_perm (none), dgates, dy_mx, dy_mxt
+    assert L.moe_combine_bwd_mx_tok(*cb, 10, 192, 2, 8, *out, s) == EUNSUP
+    assert L.moe_combine_bwd_mx_tok(*cb, 10, 256, 2, 8, *out[:3], None, s) == EINVAL
+    assert L.moe_combine_bwd_mx_tok(*cb[:2], None, *cb[3:], 10, 256, 2, 8, *out, s) == EINVAL   # null gates
+    assert L.moe_combine_bwd_mx_tok(*cb, 10, 256, 2, 8, None, None, FAKE, FAKE, s) == EINVAL    # null dgates
 
 
 def test_route_stats_validation(L):

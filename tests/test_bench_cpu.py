@@ -37,10 +37,17 @@ def test_data_movement_bytes():
     assert bench.kernel_work("dispatch", w, 2) == ("hbm", float(T * d * 2 + R * d * 2 + 4 * R))
     assert bench.kernel_work("combine", w, 2) == ("hbm", float(R * d * 2 + T * d * 2 + 8 * R))
     assert bench.kernel_work("combine_bwd", w, 2) == ("hbm", float(T * d * 2 + 2 * R * d * 2 + 12 * R))
-    # the MXFP8 dispatch also writes one E4M3 byte and 1/32 of a scale byte per element of x_perm
+    # MXFP8: the combine backward computes dgates only (dout and y_perm read, the permutation and gates read,
+    # dgates written); mx_gather reads every expert row from its token row and writes it in the rows layout and
+    # in the token-axis layout (R rows padded per expert segment to whole 32-row blocks, then to 128-token groups
+    # plus one), one E4M3 byte and 1/32 of a scale byte per element each
     w5 = wl.WORKLOADS[5]
-    base = w5.T * w5.d * 2 + w5.R * w5.d * 2 + 4 * w5.R
-    assert bench.kernel_work("dispatch", w5, 2)[1] == pytest.approx(base + w5.R * w5.d * (1 + 1 / 32))
+    T5, d5, R5, E5 = w5.T, w5.d, w5.R, w5.E
+    assert bench.kernel_work("combine_bwd", w5, 2)[1] == T5 * d5 * 2 + R5 * d5 * 2 + 12 * R5
+    rp = 128 * ((R5 // 32 + E5 + 3) // 4 + 1)
+    assert rp >= R5 + 32 * E5 // 4 and rp % 128 == 0
+    o = 1 + 1 / 32
+    assert bench.kernel_work("mx_gather", w5, 2)[1] == pytest.approx(R5 * d5 * 2 + 6 * R5 + (R5 + rp) * d5 * o)
     assert bench.kernel_work("no_such_kernel", w, 2) == ("other", 0.0)
 
 

@@ -229,6 +229,84 @@ def test_dispatch_and_combine_bwd_mx_bit_exact(gpu, T, d, E, k):
         np.testing.assert_array_equal(sc, rs)
 
 
+def _mx_tok_host(buf, R, E, d):
+    """(codes [d, Rp], scale bytes [Rp/32, d]) of a token-axis MX buffer, scales ungrouped."""
+    q, sc = B.mx_tok_split(buf, R, E, d)
+    rp = q.shape[1]
+    sc = sc.cpu().numpy().reshape(rp // 128, d, 4).transpose(0, 2, 1).reshape(rp // 32, d)
+    return q.cpu().numpy(), sc
+
+
+def _check_tok_layout(q, sc, rows, offsets, blk):
+    """Token-axis codes and scales against the oracle's segment quantiser of the bf16 expert rows: expert e's
+    blocks at positions [32 blk[e], 32 blk[e+1]), each block's tail and every position past the last block zero."""
+    rq, rs = mxo.mx_quantize(rows.astype(np.float64), axis=0, seg_offsets=offsets)
+    b = 0
+    for e in range(len(offsets) - 1):
+        lo, hi = offsets[e], offsets[e + 1]
+        assert blk[e] == b
+        for j in range(-(-(hi - lo) // 32)):
+            r0, r1 = lo + 32 * j, min(lo + 32 * j + 32, hi)
+            np.testing.assert_array_equal(q[:, 32 * b: 32 * b + (r1 - r0)], rq[r0:r1].T)
+            assert np.all(q[:, 32 * b + (r1 - r0): 32 * (b + 1)] == 0)
+            np.testing.assert_array_equal(sc[b], rs[b])
+            b += 1
+    assert b == len(rs) == blk[-1]
+    assert np.all(q[:, 32 * b:] == 0) and np.all(sc[b:] == 0)
+
+
+# (T, d, E, k, hot): hot routes most tokens to expert 0 and leaves experts empty
+TOK_CASES = [(333, 256, 8, 2, False), (1000, 2048, 128, 4, False), (77, 4096, 16, 8, False), (5, 128, 4, 1, False),
+             (700, 384, 32, 4, True), (64, 128, 1, 1, False)]
+
+
+@pytest.mark.parametrize("T,d,E,k,hot", TOK_CASES)
+def test_dispatch_and_combine_bwd_mx_tok_bit_exact(gpu, T, d, E, k, hot):
+    """The token-axis MX calls: the bf16 rows they can write equal the plain dispatch and combine backward's,
+    dgates equals the combine backward's, and both MX layouts equal the oracle's quantiser applied to those rows
+    (rows layout along d; token-axis layout down each expert segment, zero-padded)."""
+    gu.say(f"case permute MX tok T={T} d={d} E={E} k={k} hot={hot}")
+    r = np.random.default_rng(11 + T + d + E)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    if hot:
+        lg[:, 0] += 3.0
+        lg[:, E // 2:] -= 30.0        # half the experts never chosen
+    logits = torch.from_numpy(lg).cuda()
+    route = B.moe_route_topk(logits, k)
+    scale = np.exp2(r.integers(-20, 20, (T, 1))).astype(np.float32)
+    x = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32) * scale).to(torch.bfloat16).cuda()
+    y = torch.randn((T * k, d), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    dout = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32) * scale).to(torch.bfloat16).cuda()
+    xp_ref = B.moe_dispatch(x, route["perm_dst"], k)
+    dy_ref, dg_ref = B.moe_combine_bwd(dout, y, route["gates"], route["perm_dst"])
+    xp, xmx, xmxt = B.moe_dispatch_mx_tok(x, route, k, E, write_rows=True)
+    dy, dg, dymx, dymxt = B.moe_combine_bwd_mx_tok(dout, y, route["gates"], route, E, write_rows=True)
+    # without the bf16 rows: the same MX bytes
+    _, xmx2, xmxt2 = B.moe_dispatch_mx_tok(x, route, k, E)
+    _, dg2, dymx2, dymxt2 = B.moe_combine_bwd_mx_tok(dout, y, route["gates"], route, E)
+    torch.cuda.synchronize()
+    R = T * k
+    np.testing.assert_array_equal(gu.host(xp), gu.host(xp_ref))
+    np.testing.assert_array_equal(gu.host(dy), gu.host(dy_ref))
+    np.testing.assert_array_equal(dg.cpu().numpy(), dg_ref.cpu().numpy())
+    np.testing.assert_array_equal(dg2.cpu().numpy(), dg_ref.cpu().numpy())
+    for a, b in ((xmx, xmx2), (dymx, dymx2)):   # codes and scales (not the alignment gap between them)
+        for va, vb in zip(B.mx_act_split(a, R, d), B.mx_act_split(b, R, d)):
+            assert torch.equal(va, vb)
+    for a, b in ((xmxt, xmxt2), (dymxt, dymxt2)):
+        for va, vb in zip(B.mx_tok_split(a, R, E, d), B.mx_tok_split(b, R, E, d)):
+            assert torch.equal(va, vb)
+    offsets = route["offsets"].cpu().numpy()
+    blk = route["mx_blk_offsets"].cpu().numpy()
+    for mx, mxt, rows in ((xmx, xmxt, xp), (dymx, dymxt, dy)):
+        rows = rows.float().cpu().numpy()
+        q, sc = _mx_act_host(mx, R, d)
+        rq, rs = mxo.mx_quantize(rows.astype(np.float64), axis=1)
+        np.testing.assert_array_equal(q, rq)
+        np.testing.assert_array_equal(sc, rs)
+        _check_tok_layout(*_mx_tok_host(mxt, R, E, d), rows, offsets, blk)
+
+
 # (T, d, E, accumulate): E <= 8 and E <= 16 take the LDS-staged kernels (d not a
 # multiple of 512 leaves a partly filled feature group), E = 24 the generic ones
 ROUTER_CASES = [(700, 256, 8, True), (1000, 520, 6, False), (333, 1024, 16, True), (300, 264, 24, True),

@@ -66,16 +66,22 @@ def test_layer_deterministic(gpu):
 
 @pytest.mark.parametrize("name", ["mxfp8-e16", "mxfp8-big-tiles"])
 def test_mx_fused_movement_bit_identical(gpu, name):
-    """Quantising x_perm and dy_perm inside the dispatch and the combine backward (moe_dispatch_mx,
-    moe_combine_bwd_mx) gives the same bits as letting the FFN quantise them."""
+    """X and dY quantised inside the dispatch and the combine backward, in the rows layout only
+    (moe_dispatch_mx, moe_combine_bwd_mx) or in both layouts from the routing permutation
+    (moe_dispatch_mx_tok, moe_combine_bwd_mx_tok, with and without the bf16 expert rows), give the same bits as
+    letting the FFN quantise them."""
     w = SMALL[name]
     gu.say(f"case fused MX movement {name}")
     inp = wl.make_inputs(w)
-    a, step_a = gu.run_gpu_step(w, inp, mx_fused_movement=False)
-    b, step_b = gu.run_gpu_step(w, inp, mx_fused_movement=True)
-    assert step_a.x_mx is None and step_b.x_mx is not None
-    for key in a:
-        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    a, step_a = gu.run_gpu_step(w, inp, mx_movement="none")
+    assert step_a.x_mx is None
+    for movement, keep in (("rows", True), ("tok", True), ("tok", False)):
+        b, step_b = gu.run_gpu_step(w, inp, mx_movement=movement, keep_rows=keep)
+        assert step_b.x_mx is not None and (step_b.x_mxt is not None) == (movement == "tok")
+        assert (step_b.x_perm is None) == (not keep)
+        for key in b:
+            np.testing.assert_array_equal(a[key], b[key], err_msg=f"{movement} {keep} {key}")
+        assert set(a) - set(b) <= {"x_perm"}
 
 
 @pytest.mark.parametrize("name", ["mxfp8-e16", "mxfp8-big-tiles"])
