@@ -92,18 +92,17 @@ def kernel_work(name: str, w, s: int) -> tuple[str, float]:
     if w.prec == "mxfp8":
         # the combine backward computes only dgates; X and dY go to their MX layouts through mx_gather
         hbm["combine_bwd"] = T * d * s + R * d * s + 12 * R
-        # mx_gather, 2 launches (X, then dY = gate x dout): every expert row read from its token row (plus the
-        # permutation, and the gates for dY), written in the rows layout and in the token-axis layout
-        hbm["mx_gather"] = R * d * s + 6 * R + R * d * o + rp * d * o
+        # mx_gather, 4 launches, per-launch average: X and dY = gate x dout [R, d], every expert row read from its
+        # token row (plus the permutation, and the gates for dY); dHg and dHu [R, f] read in place; each written
+        # in the rows layout and in the token-axis layout
+        hbm["mx_gather"] = (2 * (R * d * s + (R + rp) * d * o) + 12 * R + 2 * (R * f * s + (R + rp) * f * o)) / 4
     if name in hbm:
         return "hbm", float(hbm[name])
     if name == "mx_quantize_rows":
-        # A, dHg, dHu [R, f] along f, one launch each; per element the source (s bytes) is read and 1 + 1/32
-        # bytes written
+        # A [R, f] along f (for G2); per element the source (s bytes) is read and 1 + 1/32 bytes written
         return "hbm", float(R * f * (s + o))
     if name == "mx_quantize_cols":
-        # A, dHg, dHu [R, f] down the tokens of each expert segment, transposed into the padded token axis:
-        # 3 launches
+        # A [R, f] down the tokens of each expert segment, transposed into the padded token axis (for G4)
         return "hbm", float(R * f * s + rp * f * o)
     if name == "mx_quantize_both":
         # one expert weight [E, d, f] per launch (3 per step): read once, written in both layouts

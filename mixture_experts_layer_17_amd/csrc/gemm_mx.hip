@@ -884,9 +884,14 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
     m.dys = dy_mx ? dy_mx + align_up(static_cast<size_t>(a.R) * a.d, 256) : b.dy.s;
     st = launch_mx_kind(kG3, m, max_tiles, s);
     if (st != MOE_OK) return st;
-    // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f
-    launch_mx_rows(a.dhg, bf, a.R, a.f, b.dhg.q, b.dhg.s, s, true);
-    launch_mx_rows(a.dhu, bf, a.R, a.f, b.dhu.q, b.dhu.s, s, true);
+    // G5: dX = dHg Wg^T + dHu Wu^T: dH along f, Wg/Wu natural [E][d][f] along f; from the same read dH along
+    // the tokens of each expert segment for the weight gradient G6
+    const uint16_t* dhg = static_cast<const uint16_t*>(a.dhg);
+    const uint16_t* dhu = static_cast<const uint16_t*>(a.dhu);
+    launch_mx_gather(dhg, a.R, a.f, 1, nullptr, nullptr, a.offsets, mx_blk_offsets, a.E, nullptr, b.dhg.q, b.dhg.s,
+                     b.dhgt.q, b.dhgt.s, s);
+    launch_mx_gather(dhu, a.R, a.f, 1, nullptr, nullptr, a.offsets, mx_blk_offsets, a.E, nullptr, b.dhu.q, b.dhu.s,
+                     b.dhut.q, b.dhut.s, s);
     if (!wcache) {
       launch_mx_rows(a.wg, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wg.q, b.wg.s, s, true);
       launch_mx_rows(a.wu, bf, static_cast<int64_t>(a.E) * a.d, a.f, b.wu.q, b.wu.s, s, true);
@@ -899,8 +904,6 @@ int mx_ffn_bwd(const FfnArgs& a, int64_t max_tiles, const int32_t* mx_blk_offset
     launch_mx_cols(a.act, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.at.q, b.at.s, s, true, mx_blk_offsets);
     if (!dy_mxt) launch_mx_cols(a.dy, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.dyt.q, b.dyt.s, s, true, mx_blk_offsets);
     if (!x_mxt) launch_mx_cols(a.x, bf, 1, a.R, a.d, a.offsets, a.E, rp, b.xt.q, b.xt.s, s, true, mx_blk_offsets);
-    launch_mx_cols(a.dhg, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhgt.q, b.dhgt.s, s, true, mx_blk_offsets);
-    launch_mx_cols(a.dhu, bf, 1, a.R, a.f, a.offsets, a.E, rp, b.dhut.q, b.dhut.s, s, true, mx_blk_offsets);
   }
   const size_t tcodes = align_up(static_cast<size_t>(a.d) * rp, 256);  // token-axis codes of a d-wide operand
   m.atq = b.at.q; m.ats = b.at.s;

@@ -299,7 +299,8 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
 }
 
 // Destination-major gather of an expert-major buffer's rows into both MX
-// layouts at once (launch_mx_gather): a workgroup takes 4 consecutive 32-row
+// layouts at once (launch_mx_gather; without a permutation, both layouts of an
+// expert-major buffer from one read): a workgroup takes 4 consecutive 32-row
 // blocks of the padded token axis (in block order, each block inside one expert
 // segment) and NSUB consecutive 64-column subtiles of them.  Each tile row names
 // its expert row and, through the routing's permutation, the token row it
@@ -368,9 +369,13 @@ __global__ __launch_bounds__(256) void mx_gather_kernel(const uint16_t* __restri
     float g = 0.f;
     if (r < b_nv[bi]) {
       row = b_r0[bi] + r;
-      const int32_t slot = perm_src[row];
-      off = static_cast<int64_t>(slot / k) * d;
-      if constexpr (SCALED) g = gates[slot];
+      if (perm_src) {
+        const int32_t slot = perm_src[row];
+        off = static_cast<int64_t>(slot / k) * d;
+        if constexpr (SCALED) g = gates[slot];
+      } else {
+        off = row * d;  // no permutation: src is the expert-major buffer itself
+      }
     }
     s_row[tid] = row;
     s_src[tid] = off;

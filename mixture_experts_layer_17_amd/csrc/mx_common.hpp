@@ -77,7 +77,8 @@ inline int64_t mx_token_rows(int64_t R, int E) { return 128 * (cdiv(cdiv(R, 32) 
 //  (codes qr [R, d], scales grouped over the R rows: word of (row, group G) at scr + 4 (G R + row)) and the
 //  token-axis layout (as launch_mx_cols with segments and grouped scales: qt [d][ldq], ldq = mx_token_rows).
 //  Expert row r holds source row perm_src[r] / k of src [T, d] (bf16), times gates[perm_src[r]] rounded to
-//  bf16 when gates is not NULL; rows_out [R, d] (bf16, may be NULL) receives the rows themselves.
+//  bf16 when gates is not NULL; without perm_src (and gates) src is the expert-major buffer [R, d] itself;
+//  rows_out [R, d] (bf16, may be NULL) receives the rows themselves.
 //  seg: nseg + 1 segment offsets, blk: their 32-row block-count prefix (device).  d % 128 == 0.
 void launch_mx_gather(const uint16_t* src, int64_t R, int d, int k, const int32_t* perm_src, const float* gates,
                       const int32_t* seg, const int32_t* blk, int nseg, uint16_t* rows_out, uint8_t* qr,

@@ -47,7 +47,12 @@ def test_data_movement_bytes():
     rp = 128 * ((R5 // 32 + E5 + 3) // 4 + 1)
     assert rp >= R5 + 32 * E5 // 4 and rp % 128 == 0
     o = 1 + 1 / 32
-    assert bench.kernel_work("mx_gather", w5, 2)[1] == pytest.approx(R5 * d5 * 2 + 6 * R5 + (R5 + rp) * d5 * o)
+    f5 = w5.f
+    per_launch = [R5 * d5 * 2 + 4 * R5 + (R5 + rp) * d5 * o,          # X: rows read from their tokens, permutation
+                  R5 * d5 * 2 + 8 * R5 + (R5 + rp) * d5 * o,          # dY: and the gates
+                  R5 * f5 * 2 + (R5 + rp) * f5 * o,                   # dHg, dHu: read in place
+                  R5 * f5 * 2 + (R5 + rp) * f5 * o]
+    assert bench.kernel_work("mx_gather", w5, 2)[1] == pytest.approx(sum(per_launch) / 4)
     assert bench.kernel_work("no_such_kernel", w, 2) == ("other", 0.0)
 
 
