@@ -411,21 +411,63 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 // ---------------------------------------------------------------------------
-// Persistent 256 x 256 MX kernel for the rows-by-expert GEMMs (G1, G2, G3, G5).
-// Workgroups loop over tiles (ids b, b + G, ... in the XCD-contiguous order),
-// and the K-steps of consecutive
-// tiles form one stream through the two LDS stages: each step's loads are
-// issued right after the barrier of the step before, and the last step of a
-// tile issues the next tile's first step, so those loads are in flight during
-// the epilogue.  Tiles are computed transposed (mfma(B, A)) so the epilogues run
-// from registers: G1 (SwiGLU) and G2 store straight from them; G3 stages its
-// Hg, Hu loads through both LDS stages (the next tile then starts after its
-// epilogue); G5 stages its rows through the stage the last step released for
-// whole-line stores.  (The weight gradients keep one workgroup per tile: a new
-// workgroup's loads do not wait for the previous tile's 128 KB of dW stores,
-// which a persistent workgroup's single vmcnt counter would; measured 21%
-// slower persistent.)
+// Persistent 256 x 256 MX kernel for the SwiGLU backward (G3) and the down
+// projection (G2).  Workgroups loop over tiles (ids b, b + G, ... in the
+// XCD-contiguous order), and the K-steps of consecutive tiles form one stream
+// through the two LDS stages: each step's loads are issued right after the
+// barrier of the step before.  Tiles are computed transposed (mfma(B, A)) so
+// the epilogues run from registers.  G2's last step issues the next tile's
+// first step, so those loads are in flight during its epilogue, which stores
+// the same number of 16-byte lines in every wave (buffer stores into a range
+// that ends with the tile's last valid row: the hardware drops the lanes past
+// it instead of the wave branching around them; tiles are whole in N, d a
+// multiple of 256); the next tile then waits for its own first loads alone,
+// which went out before these stores (loads and stores retire in issue order),
+// while the stores drain.  G3 stages its Hg, Hu loads through both LDS stages
+// (the next tile then starts after its epilogue).  Measured on the MXFP8
+// E = 128 workload: G3 621 us against 789 one workgroup per tile, G2 560
+// against 574; G1 and G5 (24-32 K-steps a tile against G2's 12) the same way
+// as G2 983 against 964 and 1002 against 994, so they keep one workgroup per
+// tile.  So do the weight gradients: a new workgroup's loads do not wait for
+// the previous tile's 128 KB of dW stores, which a persistent workgroup's
+// single vmcnt counter would (measured 21% slower persistent).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int off, const uint4& v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+}
+
+// G2's epilogue: TM x TN x 2 stores per wave.
+template <class C>
+__device__ __forceinline__ void epi_regs_store_all(const Acc<C>& acc, uint16_t* dst, int64_t ld, int rows_valid,
+                                                   int lane, int wm, int wn) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(dst, static_cast<int64_t>(rows_valid) * ld * 2);
+  const int rl = lane & 31, hc = 8 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WTM + i * 32 + rl;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      float v[2][8];
+      to_chunks(acc[i][j], v);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        bstore16(r, static_cast<int>((row * ld + wn * C::WTN + j * 32 + 16 * c + hc) * 2), pack8(v[c]));
+    }
+  }
+}
+
+// Workgroup barrier that waits for the wave's LDS accesses only: __syncthreads()
+// (whose release fence also covers LDS-DMA loads, which write LDS under the
+// vector memory counter) would make every wave wait for all its outstanding
+// vector memory operations, the next tile's loads and the epilogue's stores
+// included.  Used where the loads a step needs have been waited for explicitly
+// (wait_vm); the memory clobber keeps the compiler from moving accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 struct MxTile {
   MxKc a, b;
   int K;            // contraction length (0: zero outputs)
@@ -443,10 +485,9 @@ __device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t liv
   const FfnArgs& p = m.f;
   const int d = p.d, f = p.f;
   const int64_t wsz = static_cast<int64_t>(d) * f;
-  static_assert(KIND == kG1 || KIND == kG2 || KIND == kG3 || KIND == kG5, "rows-by-expert GEMMs");
+  static_assert(KIND == kG2 || KIND == kG3, "the persistent GEMMs");
   {
-    const int gx = KIND == kG1 ? (f + C::BN / 2 - 1) / (C::BN / 2)
-                               : KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
+    const int gx = KIND == kG3 ? (f + C::BN - 1) / C::BN : (d + C::BN - 1) / C::BN;
     const int64_t lid = xcd_tile(id, live * gx);
     if (lid < 0) return false;
     int nt;
@@ -458,16 +499,7 @@ __device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t liv
     const int64_t R = p.R;
     t.row0 = row0;
     t.rows = rows;
-    if constexpr (KIND == kG1) {
-      t.n0 = nt * (C::BN / 2);
-      t.a = MxKc{m.xq + row0 * d, nullptr, m.xs + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, R * 4};
-      const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * d;      // transposed Wg, Wu: [E][f][d]
-      const int64_t so = ee * wsz / 32 + static_cast<int64_t>(t.n0) * 4;  // scales grouped per expert over f rows
-      t.b = MxKc{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, d, 0, d, kNoSplit, f - t.n0,
-                 static_cast<int64_t>(f) * 4};
-      t.K = d;
-      t.cols = f - t.n0;
-    } else if constexpr (KIND == kG2) {
+    if constexpr (KIND == kG2) {
       t.n0 = nt * C::BN;  // over d
       t.a = MxKc{m.aq + row0 * f, nullptr, m.as + row0 * 4, nullptr, f, 0, f, kNoSplit, rows, R * 4};
       const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * f;      // transposed Wd: [E][d][f]
@@ -477,7 +509,7 @@ __device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t liv
       t.cols = d - t.n0;
       t.out = static_cast<uint16_t*>(p.o_y) + row0 * d + t.n0;
       t.ldo = d;
-    } else if constexpr (KIND == kG3) {
+    } else {  // kG3
       t.n0 = nt * C::BN;  // over f
       t.a = MxKc{m.dyq + row0 * d, nullptr, m.dys + row0 * 4, nullptr, d, 0, d, kNoSplit, rows, R * 4};
       const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * d;    // natural Wd: [E][f][d]
@@ -486,18 +518,6 @@ __device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t liv
                  static_cast<int64_t>(p.E) * f * 4};
       t.K = d;
       t.cols = f - t.n0;
-    } else {  // kG5
-      t.n0 = nt * C::BN;  // over d
-      t.a = MxKc{m.dhgq + row0 * f, m.dhuq + row0 * f, m.dhgs + row0 * 4, m.dhus + row0 * 4, f, 0, 2 * f, f, rows,
-                 R * 4};
-      const int64_t wo = ee * wsz + static_cast<int64_t>(t.n0) * f;    // natural Wg, Wu: [E][d][f]
-      const int64_t so = (ee * d + t.n0) * 4;                           // scales grouped over all E*d rows
-      t.b = MxKc{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, f, 0, 2 * f, f, d - t.n0,
-                 static_cast<int64_t>(p.E) * d * 4};
-      t.K = 2 * f;
-      t.cols = d - t.n0;
-      t.out = static_cast<uint16_t*>(p.o_dx) + row0 * d + t.n0;
-      t.ldo = d;
     }
     if (rows == 0) t.K = 0;
   }
@@ -507,8 +527,7 @@ __device__ __forceinline__ bool mx_tile(const MxArgs& m, int64_t id, int64_t liv
 // Whether hardware-order id `id` names a tile (as mx_tile, without building it).
 template <class C, int KIND>
 __device__ __forceinline__ bool mx_tile_valid(const FfnArgs& p, int64_t id, int64_t live) {
-  const int gx = KIND == kG1 ? (p.f + C::BN / 2 - 1) / (C::BN / 2)
-                             : KIND == kG3 ? (p.f + C::BN - 1) / C::BN : (p.d + C::BN - 1) / C::BN;
+  const int gx = KIND == kG3 ? (p.f + C::BN - 1) / C::BN : (p.d + C::BN - 1) / C::BN;
   return xcd_tile(id, live * gx) >= 0;
 }
 
@@ -517,8 +536,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 void ffn_mx_persistent(MxArgs m) {
   static_assert(C::BM == 256 && C::BN == 256 && C::kWaves == 8 && C::TM == 4 && C::WTN == 64,
                 "256 x 256 tiles on 8 waves of 128 x 64");
-  constexpr bool BDUAL = KIND == kG1;
   constexpr bool kStaged = KIND == kG3;
+  constexpr int kEpiOps = C::TM * C::TN * 2;  // stores of one wave's G2 epilogue (epi_regs_store_all)
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLds];
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   const FfnArgs& p = m.f;
@@ -534,31 +553,30 @@ void ffn_mx_persistent(MxArgs m) {
   uint8_t* const qa = l8;                          // A stages
   uint8_t* const qb = l8 + 2 * C::kA;              // B stages
   uint8_t* const sl = l8 + 2 * C::kA + 2 * C::kB;  // scale stages: [2 groups][A 1 KB | B 2 KB]
-  constexpr int BH = BDUAL ? C::BN / 2 : C::BN;
-  // this wave's 8 KB of stage `slot` (bf16 elements) for the staged epilogues
+  // this wave's 8 KB of stage `slot` (bf16 elements) for G3's staged epilogue
   auto stage_buf = [&](int slot) -> uint16_t* {
     return reinterpret_cast<uint16_t*>(wave < 4 ? qa + slot * C::kA + wave * 8192
                                                 : qb + slot * C::kB + (wave - 4) * 8192);
   };
   // step kt of tile t into stage `slot`: the A and B tiles and the scale runs (one per wave:
-  // group (0, 1) x {A, B half 0, B half 1}; group 1 only for K-steps that straddle two groups)
+  // group (0, 1) x {A, B}; group 1 only for K-steps that straddle two groups)
   auto issue = [&](const MxTile& t, int kt, int slot) {
     const int k0 = kt * C::BK;
     mx_dma<C, C::BM, false>(t.a, k0, qa + slot * C::kA, wave, lane);
-    mx_dma<C, C::BN, BDUAL>(t.b, k0, qb + slot * C::kB, wave, lane);
+    mx_dma<C, C::BN, false>(t.b, k0, qb + slot * C::kB, wave, lane);
     const int o = static_cast<int>((t.a.k_base / 32) & 3);
     const int grp = wave / 3, part = wave % 3;
-    if (wave < 6 && !(grp == 1 && o == 0) && !(part == 2 && !BDUAL)) {
+    if (wave < 6 && !(grp == 1 && o == 0) && part != 2) {
       const int arows = t.a.mn_valid < C::BM ? t.a.mn_valid : C::BM;
-      const int brows = t.b.mn_valid < BH ? t.b.mn_valid : BH;
-      const bool hi = !BDUAL && k0 >= t.a.ksplit;
+      const int brows = t.b.mn_valid < C::BN ? t.b.mn_valid : C::BN;
+      const bool hi = k0 >= t.a.ksplit;
       const int kk = hi ? k0 - t.a.ksplit : k0;
       const int64_t G = (t.a.k_base / 32 + kk / 32) >> 2;
       uint8_t* dst = sl + slot * C::kScaleStage + grp * 3072 + part * 1024;
       if (part == 0)
         scale_dma(hi ? t.a.s1 : t.a.s0, t.a.gs, G + grp, arows, dst, lane);
       else
-        scale_dma((part == 2 || (!BDUAL && hi)) ? t.b.s1 : t.b.s0, t.b.gs, G + grp, brows, dst, lane);
+        scale_dma(hi ? t.b.s1 : t.b.s0, t.b.gs, G + grp, brows, dst, lane);
     }
   };
 
@@ -578,8 +596,11 @@ void ffn_mx_persistent(MxArgs m) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vm<0>();
-      __syncthreads();
+      // step 0 of a tile whose loads went out during the previous tile: only the previous epilogue's stores may
+      // still be in flight after them
+      if (!kStaged && kt == 0 && pre) wait_vm<kEpiOps>();
+      else wait_vm<0>();
+      lds_barrier();
       const int slot = (g + kt) & 1;
       // the next step's loads into the other stage: this tile's, or at its last step the next tile's first
       if (kt + 1 < nk) {
@@ -609,8 +630,7 @@ void ffn_mx_persistent(MxArgs m) {
       for (int i = 0; i < C::TM; ++i) ca[i] = (word(0, wm * C::WTM + i * 32 + (lane & 31)) & msk) >> (8 * g32);
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        const int r = b_row<C, BDUAL>(wn, j) + (lane & 31);
-        cb[j] = ((BDUAL && r >= C::BN / 2 ? word(2, r - C::BN / 2) : word(1, r)) & msk) >> (8 * g32);
+        cb[j] = (word(1, b_row<C, false>(wn, j) + (lane & 31)) & msk) >> (8 * g32);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -618,7 +638,7 @@ void ffn_mx_persistent(MxArgs m) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) a[i] = mx_frag<C::BK>(as, wm * C::WTM + i * 32 + (lane & 31), ks, g32);
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) b[j] = mx_frag<C::BK>(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g32);
+        for (int j = 0; j < C::TN; ++j) b[j] = mx_frag<C::BK>(bs, b_row<C, false>(wn, j) + (lane & 31), ks, g32);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -648,14 +668,8 @@ void ffn_mx_persistent(MxArgs m) {
         g3_block<C>(acc, p, cur.row0, cur.rows, cur.n0, cur.cols, 3, b1, wm, wn, lane);
         __syncthreads();  // the LDS holds stages again
       }
-    } else if constexpr (KIND == kG5) {
-      if (nk > 0) __syncthreads();  // the last step's stage is free
-      // dX rows are read by the dispatch backward right after: ordinary stores
-      epi_staged_store<C, false>(acc, stage_buf((g + 1) & 1), cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
-    } else if constexpr (KIND == kG1) {
-      epi_regs_swiglu_fwd<C>(acc, p, cur.row0, cur.rows, cur.n0, lane, wm, wn);
     } else {  // G2: Y is read by the combine right after: ordinary stores
-      epi_regs_store<C>(acc, cur.out, cur.ldo, cur.rows, cur.cols, lane, wm, wn);
+      epi_regs_store_all<C>(acc, cur.out, cur.ldo, cur.rows, lane, wm, wn);
     }
     if (!more) break;
     mx_tile<C, KIND>(m, nid, live, cur);
@@ -699,12 +713,9 @@ int launch_mx_cfg(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
 bool mx_big_rows(int64_t R, int E) { return R >= static_cast<int64_t>(E) * 512; }
 bool mx_big_wgrad(const FfnArgs& a) { return a.d % 256 == 0 && a.f % 256 == 0; }
 
-// 256 x 256 tiles: the SwiGLU-backward GEMM (G3) on the persistent kernel, the
-// others one workgroup per tile.  Measured on the MXFP8 E = 128 workload: G3
-// persistent 763-770 us against 840 on its own 128-row table; G1, G2, G5
-// persistent 1189-1322, 679-708, 1260-1322 us against 1176-1198, 695, 1237-1240
-// per tile (their epilogues store from registers either way, so a persistent
-// workgroup gains little, and the next tile's state costs registers).
+// 256 x 256 tiles: the SwiGLU-backward GEMM (G3) and the down projection (G2)
+// on the persistent kernel, the others one workgroup per tile.  G3 persistent:
+// 621 us against 789 with one workgroup per tile (MXFP8 E = 128 workload).
 int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) {
   using C = MxBig;
   const bool wgrad = kind == kG4 || kind == kG6;
@@ -712,6 +723,13 @@ int launch_mx_kind(int kind, const MxArgs& a, int64_t max_tiles, hipStream_t s) 
   if (!big) return launch_mx_cfg<MxSmall>(kind, a, max_tiles, s);
   if (kind == kG3) {
     launch_mx_persistent<kG3>("G3_mx", a, cdiv(a.f.f, C::BN) * max_tiles, s);
+    return launch_status();
+  }
+  // G2 (12 K-steps a tile at f = 1536) persistent, its next tile's first loads in flight during the epilogue
+  // (needs whole tiles in N: its epilogue stores every column of a row).  Measured on the MXFP8 E = 128 workload:
+  // G2 574 -> 560 us; G1 and G5 (24-32 K-steps a tile) persistent the same way: 964 -> 983 and 994 -> 1002.
+  if (kind == kG2 && a.f.d % C::BN == 0) {
+    launch_mx_persistent<kG2>("G2_mx", a, cdiv(a.f.d, C::BN) * max_tiles, s);
     return launch_status();
   }
   return launch_mx_cfg<C>(kind, a, max_tiles, s);
