@@ -57,24 +57,33 @@ inline unsigned xcd_grid(int64_t total) {
 }
 
 // Rows-by-expert tile order over the live entries of the tile table times gx
-// column tiles: each expert's run of entries [T, T + n) is taken in pairs of
-// row tiles, and inside a pair the column tile is the major index, so the two
-// row tiles that read the same weight columns take consecutive logical ids
-// (hence, through xcd_tile, CUs of one XCD at about the same time) and fetch
-// those columns into its L2 once, while an expert with many row tiles still
-// works on few of them at a time (its X rows stay in L2 too).  Returns the
-// table entry and the column tile of logical id lid (< live * gx).
+// column tiles: each expert's run of entries [T, T + n) is taken in groups of
+// row tiles, and inside a group the column tile is the major index, so the row
+// tiles that read the same weight columns take consecutive logical ids (hence,
+// through xcd_tile, CUs of one XCD at about the same time) and fetch those
+// columns into its L2 once, while an expert with many row tiles still works on
+// few of them at a time (its X rows stay in L2 too).  Groups are pairs; an odd
+// run ends with a triple (n = 1: a single), so a short last row tile (an
+// expert's rows just past a multiple of the tile height) shares its weight
+// columns with the two before it instead of fetching them again alone.
+// Returns the table entry and the column tile of logical id lid (< live * gx).
 __device__ __forceinline__ int64_t expert_tile(int64_t lid, int gx, const int4* tiles, int64_t max_tiles, int& nt) {
   const int e = __builtin_amdgcn_readfirstlane(ld_uniform(tiles + lid / gx).w);
   const int4 run = ld_uniform(tiles + max_tiles + 1 + e);
   const int64_t first = __builtin_amdgcn_readfirstlane(run.x);
   const int n = __builtin_amdgcn_readfirstlane(run.y);
   const int64_t l = lid - first * gx;
-  const int64_t pair = l / (2 * gx);
-  const int m = n - 2 * pair < 2 ? 1 : 2;  // row tiles in this pair (the last of an odd run has one)
-  const int64_t l2 = l - pair * 2 * gx;
+  int64_t grp = l / (2 * gx);
+  int m = 2;  // row tiles in this group
+  if (n == 1) {
+    m = 1;
+  } else if ((n & 1) && grp >= (n - 3) / 2) {
+    grp = (n - 3) / 2;  // the closing triple: entries n - 3 .. n - 1
+    m = 3;
+  }
+  const int64_t l2 = l - grp * 2 * gx;
   nt = static_cast<int>(l2 / m);
-  return first + 2 * pair + l2 % m;
+  return first + 2 * grp + l2 % m;
 }
 
 // Weight-gradient tile order for one workgroup per tile (G4, G6), from the
