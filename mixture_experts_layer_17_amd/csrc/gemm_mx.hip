@@ -24,6 +24,7 @@
 // n = l % 32; the accumulators are laid out as in the bf16 kernels.
 #include "gemm_common.hpp"
 #include "mx_common.hpp"
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -196,6 +197,10 @@ __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, in
   const int arows = aop.mn_valid < C::BM ? aop.mn_valid : C::BM;
   constexpr int BH = BDUAL ? C::BN / 2 : C::BN;
   const int brows = bop.mn_valid < BH ? bop.mn_valid : BH;
+  // the wave's 32-row blocks of A that hold valid rows: fewer than TM only in the short last row tile of an
+  // expert, whose empty blocks skip their fragment reads and MFMAs
+  const int wrows = arows - wm * C::WTM;
+  const int tmv = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : (wrows >= C::WTM ? C::TM : (wrows + 31) / 32));
   // first block of step kt inside its matrix (K-steps of a split operand restart at the split)
   auto first_block = [&](int kt) -> int64_t {
     const int k0 = kt * BK;
@@ -226,58 +231,71 @@ __device__ __forceinline__ void mx_mainloop(const MxKc& aop, const MxKc& bop, in
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < nk) issue(s0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
-    mx_wait_steps<C::kDmaPerStep, NS - 2>(ahead);
-    __syncthreads();
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
-    const int st = kt % NS;
-    const uint8_t* as = qa + st * C::kA;
-    const uint8_t* bs = qb + st * C::kB;
-    const uint8_t* ss = sl + st * C::kScaleStage;
-    // the step's blocks from byte o of the staged group word on; those past the problem's K range get
-    // zero-weight scales
-    const int o = static_cast<int>(first_block(kt) & 3);
-    const int nb = (aop.k_valid - kt * BK) / 32;
-    const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
-    auto word = [&](int part, int row) -> uint32_t {
-      const uint32_t w0 = reinterpret_cast<const uint32_t*>(ss + part * 1024)[row];
-      if (o == 0) return w0;
-      const uint32_t w1 = reinterpret_cast<const uint32_t*>(ss + 3072 + part * 1024)[row];
-      return (w0 >> (8 * o)) | (w1 << (32 - 8 * o));
-    };
-    // lane (g, m) needs block 2 ks + g of its row for K-slice ks: the word shifted down by g bytes puts it at
-    // byte 2 ks, which the MFMA's scale operand selects (op_sel)
-    uint32_t ca[C::TM], cb[C::TN];
+  // the K loop for TMV valid row blocks of the wave (TM: a full tile; 2 covers any short last tile of up to 64
+  // rows; 0: wave rows past the valid ones, which only load and synchronise)
+  auto kloop = [&](auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+      mx_wait_steps<C::kDmaPerStep, NS - 2>(ahead);
+      __syncthreads();
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);
+      const int st = kt % NS;
+      const uint8_t* as = qa + st * C::kA;
+      const uint8_t* bs = qb + st * C::kB;
+      const uint8_t* ss = sl + st * C::kScaleStage;
+      // the step's blocks from byte o of the staged group word on; those past the problem's K range get
+      // zero-weight scales
+      const int o = static_cast<int>(first_block(kt) & 3);
+      const int nb = (aop.k_valid - kt * BK) / 32;
+      const uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - nb))));
+      auto word = [&](int part, int row) -> uint32_t {
+        const uint32_t w0 = reinterpret_cast<const uint32_t*>(ss + part * 1024)[row];
+        if (o == 0) return w0;
+        const uint32_t w1 = reinterpret_cast<const uint32_t*>(ss + 3072 + part * 1024)[row];
+        return (w0 >> (8 * o)) | (w1 << (32 - 8 * o));
+      };
+      // lane (g, m) needs block 2 ks + g of its row for K-slice ks: the word shifted down by g bytes puts it at
+      // byte 2 ks, which the MFMA's scale operand selects (op_sel)
+      uint32_t ca[C::TM], cb[C::TN];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) ca[i] = (word(0, wm * C::WTM + i * 32 + (lane & 31)) & m) >> (8 * g);
+      for (int i = 0; i < C::TM; ++i) ca[i] = (word(0, wm * C::WTM + i * 32 + (lane & 31)) & m) >> (8 * g);
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int r = b_row<C, BDUAL>(wn, j) + (lane & 31);
-      cb[j] = ((BDUAL && r >= C::BN / 2 ? word(2, r - C::BN / 2) : word(1, r)) & m) >> (8 * g);
+      for (int j = 0; j < C::TN; ++j) {
+        const int r = b_row<C, BDUAL>(wn, j) + (lane & 31);
+        cb[j] = ((BDUAL && r >= C::BN / 2 ? word(2, r - C::BN / 2) : word(1, r)) & m) >> (8 * g);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NSL; ++ks) {
+        i32x8 a[TMV > 0 ? TMV : 1], b[C::TN];
+#pragma unroll
+        for (int i = 0; i < TMV; ++i) a[i] = mx_frag<BK>(as, wm * C::WTM + i * 32 + (lane & 31), ks, g);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) b[j] = mx_frag<BK>(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g);
+#pragma unroll
+        for (int i = 0; i < TMV; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j) {
+            const int sa = static_cast<int>(ca[i]), sb = static_cast<int>(cb[j]);
+            // TR: the tile transposed (B in the first operand slot), so a lane holds four consecutive output
+            // columns of one row (the register-direct and wave-staged epilogues)
+            if (ks == 0)
+              acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, sb, 0, sa)
+                             : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa, 0, sb);
+            else
+              acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 2, sb, 2, sa)
+                             : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 2, sa, 2, sb);
+          }
+      }
     }
-#pragma unroll
-    for (int ks = 0; ks < NSL; ++ks) {
-      i32x8 a[C::TM], b[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) a[i] = mx_frag<BK>(as, wm * C::WTM + i * 32 + (lane & 31), ks, g);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) b[j] = mx_frag<BK>(bs, b_row<C, BDUAL>(wn, j) + (lane & 31), ks, g);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-          const int sa = static_cast<int>(ca[i]), sb = static_cast<int>(cb[j]);
-          // TR: the tile transposed (B in the first operand slot), so a lane holds four consecutive output
-          // columns of one row (the register-direct and wave-staged epilogues)
-          if (ks == 0)
-            acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, sb, 0, sa)
-                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa, 0, sb);
-          else
-            acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 2, sb, 2, sa)
-                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 2, sa, 2, sb);
-        }
-    }
+  };
+  if (tmv > 2 || C::TM <= 2) {
+    if (tmv > 0) kloop(std::integral_constant<int, C::TM>{});
+    else kloop(std::integral_constant<int, 0>{});
+  } else if (tmv > 0) {
+    kloop(std::integral_constant<int, (C::TM < 2 ? C::TM : 2)>{});
+  } else {
+    kloop(std::integral_constant<int, 0>{});
   }
   __syncthreads();  // the epilogue reuses the LDS
 }
