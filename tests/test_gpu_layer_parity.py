@@ -38,6 +38,9 @@ SMALL = {
     "mxfp8-e128": wl.scaled(W[5], T=1536, d=256, f=256),
     # >= 1024 rows per expert and d, f multiples of 256: the 256 x 256 MX tiles, ragged segment ends
     "mxfp8-big-tiles": wl.scaled(W[5], T=2300, d=512, f=256, E=2, k=1),
+    # 569 and 581 rows: three 256-row tiles per expert taken as one triple, last tiles of 57 and 69 rows (the K loop
+    # for at most two valid 32-row blocks per wave, and the full one)
+    "mxfp8-short-tails": wl.scaled(W[5], T=1150, d=512, f=256, E=2, k=1),
 }
 
 
