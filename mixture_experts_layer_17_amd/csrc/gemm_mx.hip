@@ -14,9 +14,11 @@
 // The fp8 tiles (K-step of 128 bytes per row) move into LDS with the gfx950
 // LDS-DMA buffer loads, 16-byte chunks XOR-swizzled by row as in the bf16
 // kernels; the E8M0 scales (one 32-bit word of four blocks per tile row and
-// K-step) are fetched one K-step ahead, one tile row per thread, and staged in LDS.  Where a K-step runs past the end of an
-// expert's token range both operands' scales are set to 2^-127, so whatever
-// finite codes lie there contribute exactly zero (products below 2^-200).
+// K-step, grouped so that a tile's words for one K-step are 1 KB in a row) come
+// with the data, one 1 KB LDS-DMA run per operand (half) and K-step, and are
+// staged in LDS.  Where a K-step runs past the end of an expert's token range
+// both operands' scales are set to 2^-127, so whatever finite codes lie there
+// contribute exactly zero (products below 2^-200).
 // MFMA operand layout (32x32x64 f8, checked on the hardware): lane l =
 // (g = l/32, m = l%32) supplies A[m][16g .. 16g+15] in its first 16 bytes and
 // A[m][32+16g .. 32+16g+15] in its last 16; its scale operand is the E8M0 scale
