@@ -310,7 +310,76 @@ struct MxArgs {
   const uint8_t *xq, *xs, *aq, *as, *dyq, *dys, *dhgq, *dhgs, *dhuq, *dhus;          // row-blocked [R, K]
   const uint8_t *wgq, *wgs, *wuq, *wus, *wdq, *wds;                                   // weights, K-contiguous
   const uint8_t *xtq, *xts, *dytq, *dyts, *atq, *ats, *dhgtq, *dhgts, *dhutq, *dhuts;  // [cols, ldt]
+  uint8_t *oaq, *oas;  // G1 on 256 x 256 tiles: A's rows layout (G2's operand), written by its epilogue
 };
+
+// G1's register-direct epilogue (as epi_regs_swiglu_fwd: Hg, Hu and A = silu(Hg) * Hu
+// as bf16) that also encodes A into its MX rows layout for G2 (codes [R][f],
+// grouped scales), so no separate pass reads A back.  Each wave's 32-column
+// slice of the tile is one 32-element block of every row: a lane holds 16 of
+// its values (to_chunks), lane l ^ 32 the other 16.  The block is encoded from
+// A rounded to bf16, the values the quantiser would read, with its arithmetic,
+// so the bytes equal its output.
+template <class C>
+__device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const FfnArgs& p, int64_t row0, int rows,
+                                                       int n0, int lane, int wm, int wn, uint8_t* aq, uint8_t* as) {
+  constexpr int H = C::TN / 2;
+  static_assert(C::WTN / 2 == 32 * H, "one 32-column block per fragment column");
+  const int rl = lane & 31, h = lane >> 5, hc = 8 * h;
+  const int64_t f = p.f, R = p.R;
+  uint16_t* hg = static_cast<uint16_t*>(p.o_hg) + row0 * f + n0;
+  uint16_t* hu = static_cast<uint16_t*>(p.o_hu) + row0 * f + n0;
+  uint16_t* ac = static_cast<uint16_t*>(p.o_act) + row0 * f + n0;
+  uint8_t* q = aq + row0 * f + n0;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WTM + i * 32 + rl;
+    const bool rv = row < rows;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      float g[2][8], u[2][8];
+      to_chunks(acc[i][j], g);
+      to_chunks(acc[i][j + H], u);
+      uint4 ab[2];
+      float v[2][8];
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float a[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a[t] = silu_f(g[c][t]) * u[c][t];
+        ab[c] = pack8(a);
+        Elem<uint16_t>::unpack(ab[c], v[c]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(v[c][t]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int e = mx_block_exponent(amax);
+      const float inv = mx_inv_scale(e);
+      const int col = wn * (C::WTN / 2) + j * 32;  // the block's first column in the tile
+      // codes of the lane's two runs of eight (columns 16c + 8h ..)
+      uint2 cw[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        cw[c] = make_uint2(e4m3_pack4(v[c][0] * inv, v[c][1] * inv, v[c][2] * inv, v[c][3] * inv),
+                           e4m3_pack4(v[c][4] * inv, v[c][5] * inv, v[c][6] * inv, v[c][7] * inv));
+      if (rv) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int64_t o = row * f + col + 16 * c + hc;
+          store16<false>(hg + o, pack8(g[c]));
+          store16<false>(hu + o, pack8(u[c]));
+          store16<false>(ac + o, ab[c]);
+          *reinterpret_cast<uint2*>(q + o) = cw[c];
+        }
+        if (h == 0) {
+          const int64_t b = (n0 + col) / 32;  // the block's index along f
+          as[((b >> 2) * R + row0 + row) * 4 + (b & 3)] = static_cast<uint8_t>(e + 127);
+        }
+      }
+    }
+  }
+}
 
 template <class C, int KIND>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_mx_kernel(MxArgs m) {
@@ -347,7 +416,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
       const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, d, 0, d, kNoSplit, f - n0,
                    static_cast<int64_t>(f) * 4};
       mx_mainloop<C, true, TR>(a, b, d, lds8, tid, acc);
-      if constexpr (TR) epi_regs_swiglu_fwd<C>(acc, p, row0, rows, n0, lane, wm, wn);
+      if constexpr (TR) epi_regs_swiglu_fwd_mx<C>(acc, p, row0, rows, n0, lane, wm, wn, m.oaq, m.oas);
       else epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else if constexpr (KIND == kG2) {
       const int n0 = nt * C::BN;  // over d
@@ -888,9 +957,11 @@ int mx_ffn_fwd(const FfnArgs& a, int64_t max_tiles, const char* wcache, const ui
   }
   m.xq = x_mx ? x_mx : b.x.q;
   m.xs = x_mx ? x_mx + align_up(static_cast<size_t>(a.R) * a.d, 256) : b.x.s;
+  // A along f for G2: encoded by G1's epilogue on 256 x 256 tiles, else by the quantiser from the stored A
+  m.oaq = b.a.q; m.oas = b.a.s;
   int st = launch_mx_kind(kG1, m, max_tiles, s);
   if (st != MOE_OK) return st;
-  launch_mx_rows(a.o_act, bf, a.R, a.f, b.a.q, b.a.s, s, true);
+  if (ffn_mx_bm(a.R, a.E) != MxBig::BM) launch_mx_rows(a.o_act, bf, a.R, a.f, b.a.q, b.a.s, s, true);
   m.aq = b.a.q; m.as = b.a.s;
   return launch_mx_kind(kG2, m, max_tiles, s);
 }

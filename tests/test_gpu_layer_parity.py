@@ -212,3 +212,38 @@ def test_mx_forward_gemm_matches_dequantised_operands(gpu):
     gu.say(f"  mx gemm G1 vs dequantised-operand product: {err:.2e}")
     # bf16 output rounding (2^-9 relative) and the matrix core's own accumulation
     assert err <= 4e-3
+
+
+def test_mx_down_gemm_matches_dequantised_operands_fused_act(gpu):
+    """On 256 x 256 tiles G1's epilogue encodes A for G2 itself (no quantiser pass over the stored A): the MX
+    down GEMM equals the fp64 product of the oracle's quantise -> dequantise of the GPU's own bf16 A (along f)
+    and of W_down, up to the bf16 rounding of its output.  A misplaced code or scale byte shows well above that."""
+    from mixture_experts_layer_17_amd import binding as B
+    w = wl.scaled(W[5], T=2300, d=512, f=256, E=2, k=1)  # >= 512 rows per expert: the 256 x 256 tiles
+    gu.say("case mx down gemm with the fused A encoding")
+    inp = wl.make_inputs(w)
+    idx = mo.topk_select(inp["logits"], w.k)
+    meta = mo.routing_metadata(idx, w.E)
+    xp = inp["x"][meta["perm_src"] // w.k]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    out = B.moe_grouped_ffn_fwd(dev(xp), torch.from_numpy(meta["offsets"]).cuda(), dev(inp["w_gate"]),
+                                dev(inp["w_up"]), dev(inp["w_down"]), "mxfp8")
+    torch.cuda.synchronize()
+    a = gu.host(out["a_act"]).astype(np.float64)
+    y = gu.host(out["y_perm"])
+    aq = mxl.q_along(a, 1)
+    ref = np.zeros(y.shape)
+    mag = np.zeros(y.shape)  # sum over f of |a_q w_q|: the scale of the fp32 accumulation's rounding
+    off = meta["offsets"]
+    for e in range(w.E):
+        s = slice(int(off[e]), int(off[e + 1]))
+        wq = mxl.q_along(np.asarray(inp["w_down"][e], np.float64), 0)
+        ref[s] = aq[s] @ wq
+        mag[s] = np.abs(aq[s]) @ np.abs(wq)
+    err = gu.rel_err(y, ref)
+    gu.say(f"  mx gemm G2 (A encoded by G1) vs dequantised-operand product: {err:.2e}")
+    assert err <= 4e-3
+    # element by element: the output's bf16 rounding (2^-9 relative) with room for the accumulation order; a
+    # scale byte or an 8-column run of codes in the wrong place moves whole rows far past this
+    bad = np.abs(y - ref) > 2.0**-8 * np.abs(ref) + 2.0**-12 * mag
+    assert not bad.any(), f"{int(bad.sum())} outputs off, first at {np.argwhere(bad)[0]}"
