@@ -353,7 +353,10 @@ __device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const 
 #pragma unroll
         for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(v[c][t]));
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      {  // with lane l ^ 32 (the row's other 16 values): a VALU lane swap, no LDS round trip
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
       const int e = mx_block_exponent(amax);
       const float inv = mx_inv_scale(e);
       const int col = wn * (C::WTN / 2) + j * 32;  // the block's first column in the tile
