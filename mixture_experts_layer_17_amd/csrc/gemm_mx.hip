@@ -313,16 +313,35 @@ struct MxArgs {
   uint8_t *oaq, *oas;  // G1 on 256 x 256 tiles: A's rows layout (G2's operand), written by its epilogue
 };
 
+// Workgroup barrier that waits for the wave's LDS accesses only: __syncthreads()
+// (whose release fence also covers LDS-DMA loads, which write LDS under the
+// vector memory counter) would make every wave wait for all its outstanding
+// vector memory operations, the next tile's loads and the epilogue's stores
+// included.  Used where the loads a step needs have been waited for explicitly
+// (wait_vm); the memory clobber keeps the compiler from moving accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // G1's register-direct epilogue (as epi_regs_swiglu_fwd: Hg, Hu and A = silu(Hg) * Hu
 // as bf16) that also encodes A into its MX rows layout for G2 (codes [R][f],
 // grouped scales), so no separate pass reads A back.  Each wave's 32-column
 // slice of the tile is one 32-element block of every row: a lane holds 16 of
 // its values (to_chunks), lane l ^ 32 the other 16.  The block is encoded from
 // A rounded to bf16, the values the quantiser would read, with its arithmetic,
-// so the bytes equal its output.
+// so the bytes equal its output.  The tile's 128 columns (n0 a multiple of 128)
+// are whole 128-byte code lines and whole scale words (one block group), so
+// codes and scale bytes are gathered in the idle LDS and leave as whole lines
+// and one 1 KB run of words: stored from registers, the 16-byte pieces of 32
+// rows per instruction cost G1 about 4% (measured).
 template <class C>
 __device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const FfnArgs& p, int64_t row0, int rows,
-                                                       int n0, int lane, int wm, int wn, uint8_t* aq, uint8_t* as) {
+                                                       int n0, int lane, int wm, int wn, int wave, uint8_t* aq,
+                                                       uint8_t* as, uint8_t* stage) {
+  static_assert(C::BN / 2 == 128 && C::BM * 4 <= 1024 * 4, "a tile's codes are 128-byte lines, its scales 1 KB");
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  uint8_t* sq = stage;                  // [BM][128] codes, 16-byte chunks XOR-swizzled by row
+  uint8_t* sw = stage + C::BM * 128;    // [BM] scale words
   constexpr int H = C::TN / 2;
   static_assert(C::WTN / 2 == 32 * H, "one 32-column block per fragment column");
   const int rl = lane & 31, h = lane >> 5, hc = 8 * h;
@@ -330,7 +349,6 @@ __device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const 
   uint16_t* hg = static_cast<uint16_t*>(p.o_hg) + row0 * f + n0;
   uint16_t* hu = static_cast<uint16_t*>(p.o_hu) + row0 * f + n0;
   uint16_t* ac = static_cast<uint16_t*>(p.o_act) + row0 * f + n0;
-  uint8_t* q = aq + row0 * f + n0;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int row = wm * C::WTM + i * 32 + rl;
@@ -366,6 +384,12 @@ __device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const 
       for (int c = 0; c < 2; ++c)
         cw[c] = make_uint2(e4m3_pack4(v[c][0] * inv, v[c][1] * inv, v[c][2] * inv, v[c][3] * inv),
                            e4m3_pack4(v[c][4] * inv, v[c][5] * inv, v[c][6] * inv, v[c][7] * inv));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x2 w2 = {cw[c].x, cw[c].y};
+        *reinterpret_cast<u32x2*>(sq + row * 128 + ((((col >> 4) + c) ^ (row & 7)) << 4) + hc) = w2;
+      }
+      if (h == 0) sw[row * 4 + col / 32] = static_cast<uint8_t>(e + 127);  // byte (block within the group)
       if (rv) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -373,13 +397,28 @@ __device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const 
           store16<false>(hg + o, pack8(g[c]));
           store16<false>(hu + o, pack8(u[c]));
           store16<false>(ac + o, ab[c]);
-          *reinterpret_cast<uint2*>(q + o) = cw[c];
-        }
-        if (h == 0) {
-          const int64_t b = (n0 + col) / 32;  // the block's index along f
-          as[((b >> 2) * R + row0 + row) * 4 + (b & 3)] = static_cast<uint8_t>(e + 127);
         }
       }
+    }
+  }
+  lds_barrier();  // the staged codes and scale bytes of all waves (the bf16 stores stay in flight)
+  // wave w: rows 32w .. 32w + 31, eight lanes (one 128-byte line) per row
+#pragma unroll
+  for (int t = 0; t < C::BM / 8 / C::kWaves; ++t) {
+    const int rr = (wave * (C::BM / 8 / C::kWaves) + t) * 8 + (lane >> 3), k = lane & 7;
+    if (rr < rows) {
+      const uint4 v = lds_get16(sq + rr * 128 + ((k ^ (rr & 7)) << 4));
+      *reinterpret_cast<uint4*>(aq + (row0 + rr) * f + n0 + 16 * k) = v;
+    }
+  }
+  // the words of the tile's rows for block group n0 / 128: rows row0 .. row0 + rows - 1, contiguous
+  // (4-byte aligned only: the run starts at any row), 256 bytes per store instruction
+  if (wave == C::kWaves - 1) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(as + ((n0 / 128) * R + row0) * 4);
+#pragma unroll
+    for (int t = 0; t < C::BM / 64; ++t) {
+      const int r = t * 64 + lane;
+      if (r < rows) dst[r] = reinterpret_cast<const uint32_t*>(sw)[r];
     }
   }
 }
@@ -419,7 +458,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(2))
       const MxKc b{m.wgq + wo, m.wuq + wo, m.wgs + so, m.wus + so, d, 0, d, kNoSplit, f - n0,
                    static_cast<int64_t>(f) * 4};
       mx_mainloop<C, true, TR>(a, b, d, lds8, tid, acc);
-      if constexpr (TR) epi_regs_swiglu_fwd_mx<C>(acc, p, row0, rows, n0, lane, wm, wn, m.oaq, m.oas);
+      if constexpr (TR) epi_regs_swiglu_fwd_mx<C>(acc, p, row0, rows, n0, lane, wm, wn, wave, m.oaq, m.oas, lds8);
       else epi_swiglu_fwd<C>(acc, lds, p, row0, rows, n0, tid);
     } else if constexpr (KIND == kG2) {
       const int n0 = nt * C::BN;  // over d
@@ -548,16 +587,6 @@ __device__ __forceinline__ void epi_regs_store_all(const Acc<C>& acc, uint16_t* 
         bstore16(r, static_cast<int>((row * ld + wn * C::WTN + j * 32 + 16 * c + hc) * 2), pack8(v[c]));
     }
   }
-}
-
-// Workgroup barrier that waits for the wave's LDS accesses only: __syncthreads()
-// (whose release fence also covers LDS-DMA loads, which write LDS under the
-// vector memory counter) would make every wave wait for all its outstanding
-// vector memory operations, the next tile's loads and the epilogue's stores
-// included.  Used where the loads a step needs have been waited for explicitly
-// (wait_vm); the memory clobber keeps the compiler from moving accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 struct MxTile {
