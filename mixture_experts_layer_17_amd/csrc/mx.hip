@@ -398,6 +398,10 @@ __global__ __launch_bounds__(256) void mx_gather_kernel(const uint16_t* __restri
   };
   uint4 nxt[NV];
   load(bx * NSUB * kColW, nxt);
+  // rows layout: the low half of each row's group word (blocks of the even subtile), stored whole, as one
+  // 4-byte word, with the odd subtile's half (2-byte pieces were half-sector writes)
+  uint32_t pend[2] = {0u, 0u};
+  static_assert(NSUB % 2 == 0, "subtile pairs make whole scale groups");
 #pragma unroll 1
   for (int sub = 0; sub < NSUB; ++sub) {
     const int64_t c0 = (bx * NSUB + sub) * kColW;
@@ -488,8 +492,13 @@ __global__ __launch_bounds__(256) void mx_gather_kernel(const uint16_t* __restri
           static_cast<uint32_t>(e + 127) | (static_cast<uint32_t>(__shfl_xor(e, 2, 64) + 127) << 8);
       if (row >= 0) {
         *reinterpret_cast<uint4*>(qr + row * d + c0 + qq * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-        if (qq == 0)
-          *reinterpret_cast<uint16_t*>(scr + scale_index(true, row, c0 / 32, R, d / 32)) = static_cast<uint16_t>(pair);
+        if (qq == 0) {
+          if ((sub & 1) == 0)
+            pend[h] = pair;
+          else
+            *reinterpret_cast<uint32_t*>(scr + scale_index(true, row, (c0 - kColW) / 32, R, d / 32)) =
+                pend[h] | (pair << 16);
+        }
       }
     }
   }
