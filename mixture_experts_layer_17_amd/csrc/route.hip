@@ -35,12 +35,24 @@ constexpr int kScanBatch = 8;    // block counts per thread loaded before any is
 // so the lower expert index keeps the earlier slot.
 __device__ __forceinline__ bool ranks_above(float a, float b) { return a > b || (b != b && a == a); }
 
+// The selection's total order: a before b when a ranks above b, or neither
+// ranks above the other and a has the lower expert index.
+__device__ __forceinline__ bool before(float av, int ai, float bv, int bi) {
+  return ranks_above(av, bv) || (!ranks_above(bv, av) && ai < bi);
+}
+
+// P lanes per token (1, 2 or 4, and at least K experts each): lane p of a token
+// scans the experts [p E / P, (p + 1) E / P) in index order with the insertion
+// rule below, and the P sorted lists then meet over lane shuffles, each lane
+// inserting its partner's entries into its own list under the total order.
+// The top K of a row under that (strict) order is unique, so the result does
+// not depend on P.  A workgroup still takes 64 tokens (one mask bit each).
 template <int K>
-__global__ __launch_bounds__(64) void route_select_kernel(const float* __restrict__ logits, int64_t T,
-                                                          int E, int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ gates,
-                                                          int32_t* __restrict__ rank,
-                                                          int32_t* __restrict__ blk_counts) {
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits, int64_t T,
+                                                           int E, int P, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ gates,
+                                                           int32_t* __restrict__ rank,
+                                                           int32_t* __restrict__ blk_counts) {
   extern __shared__ float smem[];
   // For E <= kStageMaxE the [64, E] logit tile is staged through LDS with
   // coalesced loads (odd row stride: lane-private rows hit distinct banks);
@@ -50,28 +62,29 @@ __global__ __launch_bounds__(64) void route_select_kernel(const float* __restric
   float* tile = smem;
   unsigned long long* mask =
       reinterpret_cast<unsigned long long*>(smem + (stage ? kTokPerBlk * ld : 0));
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, nthr = blockDim.x;  // 64 P threads
+  const int tok = tid / P, part = tid - tok * P;   // the block's token (0 .. 63) and the part of its row
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlk;
   const int ntok = static_cast<int>(T - t0 < kTokPerBlk ? T - t0 : kTokPerBlk);
 
   const float* src = logits + t0 * E;
   if (stage) {
-    // 16-byte loads, kStageBatch per lane issued before any is written to LDS
+    // 16-byte loads, kStageBatch per thread issued before any is written to LDS
     // (src is 16-byte aligned when logits is: t0 * E * 4 is a multiple of 256)
     const int nel = ntok * E;
     const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
     const int nv = vec ? nel / 4 : 0;
     const float4* s4 = reinterpret_cast<const float4*>(src);
-    for (int v0 = 0; v0 < nv; v0 += 64 * kStageBatch) {
+    for (int v0 = 0; v0 < nv; v0 += nthr * kStageBatch) {
       float4 buf[kStageBatch];
 #pragma unroll
       for (int u = 0; u < kStageBatch; ++u) {
-        const int v = v0 + u * 64 + lane;
+        const int v = v0 + u * nthr + tid;
         if (v < nv) buf[u] = s4[v];
       }
 #pragma unroll
       for (int u = 0; u < kStageBatch; ++u) {
-        const int v = v0 + u * 64 + lane;
+        const int v = v0 + u * nthr + tid;
         if (v < nv) {
           int r = (4 * v) / E, c = 4 * v - r * E;
           const float f[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
@@ -83,30 +96,33 @@ __global__ __launch_bounds__(64) void route_select_kernel(const float* __restric
         }
       }
     }
-    for (int i = 4 * nv + lane; i < nel; i += 64) {
+    for (int i = 4 * nv + tid; i < nel; i += nthr) {
       const int r = i / E;
       tile[r * ld + (i - r * E)] = src[i];
     }
   }
-  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
+  for (int e = tid; e < E; e += nthr) mask[e] = 0ull;
   __syncthreads();
 
+  const bool live = tok < ntok;
   float val[K];
   int idx[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) { val[i] = 0.f; idx[i] = i; }
 
-  if (lane < ntok) {
-    const float* row = stage ? tile + lane * ld : src + static_cast<int64_t>(lane) * E;
-    for (int e = 0; e < E; ++e) {
+  if (live) {
+    const float* row = stage ? tile + tok * ld : src + static_cast<int64_t>(tok) * E;
+    const int e0 = part * E / P, e1 = (part + 1) * E / P;
+    for (int e = e0; e < e1; ++e) {
       const float v = row[e];
       // Candidate e has a larger index than every entry held, so it goes in
       // front of an entry only when it ranks strictly above it.  The first K
-      // experts fill the list unconditionally; entries are never duplicated, so
-      // the result is K distinct valid experts for any input.
-      const bool take = (e < K) || ranks_above(v, val[K - 1]);
+      // experts of the part fill the list unconditionally; entries are never
+      // duplicated, so the result is K distinct valid experts for any input.
+      const int q = e - e0;
+      const bool take = (q < K) || ranks_above(v, val[K - 1]);
       if (take) {
-        const int pos = e < K ? e : K - 1;
+        const int pos = q < K ? q : K - 1;
 #pragma unroll
         for (int i = 0; i < K; ++i)
           if (i == pos) { val[i] = v; idx[i] = e; }
@@ -119,29 +135,55 @@ __global__ __launch_bounds__(64) void route_select_kernel(const float* __restric
         }
       }
     }
+  }
+  // the parts' lists meet (lanes tok P .. tok P + P - 1 share a wave); every lane of a token ends with its top K
+  for (int m = 1; m < P; m <<= 1) {
+    float pv[K];
+    int pi[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      pv[i] = __shfl_xor(val[i], m, 64);
+      pi[i] = __shfl_xor(idx[i], m, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (before(pv[j], pi[j], val[K - 1], idx[K - 1])) {
+        val[K - 1] = pv[j];
+        idx[K - 1] = pi[j];
+#pragma unroll
+        for (int i = K - 1; i >= 1; --i) {
+          if (before(val[i], idx[i], val[i - 1], idx[i - 1])) {
+            const float tv = val[i]; val[i] = val[i - 1]; val[i - 1] = tv;
+            const int ti = idx[i]; idx[i] = idx[i - 1]; idx[i - 1] = ti;
+          }
+        }
+      }
+    }
+  }
+  if (live && part == 0) {
     // Renormalised gates: softmax over the K chosen logits.
     float z[K];
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < K; ++i) { z[i] = __expf(val[i] - val[0]); s += z[i]; }
     const float inv = 1.0f / s;
-    const int64_t t = t0 + lane;
+    const int64_t t = t0 + tok;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       topk_idx[t * K + i] = idx[i];
       gates[t * K + i] = z[i] * inv;
-      atomicOr(&mask[idx[i]], 1ull << lane);
+      atomicOr(&mask[idx[i]], 1ull << tok);
     }
   }
   __syncthreads();
-  if (lane < ntok) {
-    const unsigned long long below = (1ull << lane) - 1ull;
-    const int64_t t = t0 + lane;
+  if (live && part == 0) {
+    const unsigned long long below = (1ull << tok) - 1ull;
+    const int64_t t = t0 + tok;
 #pragma unroll
     for (int i = 0; i < K; ++i) rank[t * K + i] = __popcll(mask[idx[i]] & below);
   }
   int32_t* cnt = blk_counts + static_cast<int64_t>(blockIdx.x) * E;
-  for (int e = lane; e < E; e += 64) cnt[e] = __popcll(mask[e]);
+  for (int e = tid; e < E; e += nthr) cnt[e] = __popcll(mask[e]);
 }
 
 // One workgroup.  blk_base has the layout of blk_counts and is written in place.
@@ -280,8 +322,9 @@ void launch_select(const float* logits, int64_t T, int E, int32_t* idx, float* g
   const int64_t nblk = cdiv(T, kTokPerBlk);
   const size_t tile = E <= kStageMaxE ? static_cast<size_t>(kTokPerBlk) * (E + 1) * sizeof(float) : 0;
   const size_t lds = tile + static_cast<size_t>(E) * 8;
-  MOE_LAUNCH("route_select", route_select_kernel<K>, dim3(static_cast<unsigned>(nblk)), dim3(64), lds, s, logits,
-                     T, E, idx, gates, rank, blk);
+  const int P = E >= 4 * K ? 4 : (E >= 2 * K ? 2 : 1);  // lanes per token, at least K experts each
+  MOE_LAUNCH("route_select", route_select_kernel<K>, dim3(static_cast<unsigned>(nblk)), dim3(64 * P), lds, s, logits,
+                     T, E, P, idx, gates, rank, blk);
 }
 
 template <int K>
