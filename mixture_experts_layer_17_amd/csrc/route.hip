@@ -281,34 +281,44 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __res
   perm_src[row] = static_cast<int32_t>(i);
 }
 
-// dlogits[t, e] = g_j (dg_j - sum_i g_i dg_i) if e = S_j, else 0.
-template <int K>
+// dlogits[t, e] = g_j (dg_j - sum_i g_i dg_i) if e = S_j, else 0.  A thread
+// takes V consecutive experts of one token (V = 4: one 16-byte store) and
+// reads the token's K gates, gate gradients and indices once.
+template <int K, int V>
 __global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict__ gates,
                                                         const float* __restrict__ dgates,
                                                         const int32_t* __restrict__ topk_idx, int64_t T,
                                                         int E, float* __restrict__ dlogits) {
+  const int ev = E / V;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= T * E) return;
-  const int64_t t = i / E;
-  const int e = static_cast<int>(i - t * E);
-  float inner = 0.f, mine = 0.f;
+  if (i >= T * ev) return;
+  const int64_t t = i / ev;
+  const int e0 = static_cast<int>(i - t * ev) * V;
+  float g[K], dg[K];
+  int id[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const float g = gates[t * K + j], dg = dgates[t * K + j];
-    inner += g * dg;
+    g[j] = gates[t * K + j];
+    dg[j] = dgates[t * K + j];
+    id[j] = topk_idx[t * K + j];
   }
+  float inner = 0.f;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    if (topk_idx[t * K + j] == e) {
-      const float g = gates[t * K + j], dg = dgates[t * K + j];
-      mine = g * (dg - inner);
-    }
+  for (int j = 0; j < K; ++j) inner += g[j] * dg[j];
+  float out[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    // an unselected expert gets exactly zero
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (id[j] == e0 + v) mine = g[j] * (dg[j] - inner);
+    out[v] = mine;
   }
-  // An unselected expert gets exactly zero.
-  bool sel = false;
-#pragma unroll
-  for (int j = 0; j < K; ++j) sel |= topk_idx[t * K + j] == e;
-  dlogits[i] = sel ? mine : 0.f;
+  if constexpr (V == 4)
+    *reinterpret_cast<float4*>(dlogits + t * E + e0) = make_float4(out[0], out[1], out[2], out[3]);
+  else
+    dlogits[t * E + e0] = out[0];
 }
 
 size_t route_ws_bytes(int64_t T, int E, int k) {
@@ -330,9 +340,15 @@ void launch_select(const float* logits, int64_t T, int E, int32_t* idx, float* g
 template <int K>
 void launch_bwd(const float* g, const float* dg, const int32_t* idx, int64_t T, int E, float* dl,
                 hipStream_t s) {
-  const int64_t n = T * E;
-  MOE_LAUNCH("route_topk_bwd", route_bwd_kernel<K>, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, g, dg,
-                     idx, T, E, dl);
+  if (E % 4 == 0 && (reinterpret_cast<uintptr_t>(dl) & 15u) == 0) {
+    const int64_t n = T * (E / 4);
+    MOE_LAUNCH("route_topk_bwd", (route_bwd_kernel<K, 4>), dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s,
+               g, dg, idx, T, E, dl);
+  } else {
+    const int64_t n = T * E;
+    MOE_LAUNCH("route_topk_bwd", (route_bwd_kernel<K, 1>), dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s,
+               g, dg, idx, T, E, dl);
+  }
 }
 
 bool route_args_ok(int64_t T, int E, int k) {
