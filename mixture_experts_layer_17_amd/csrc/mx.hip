@@ -396,19 +396,19 @@ __global__ __launch_bounds__(256) void mx_gather_kernel(const uint16_t* __restri
       out[i] = off >= 0 ? *reinterpret_cast<const uint4*>(src + off + c0 + cv * VEC) : make_uint4(0, 0, 0, 0);
     }
   };
-  uint4 nxt[NV];
-  load(bx * NSUB * kColW, nxt);
+  uint4 all[NSUB][NV];  // every subtile's loads in flight at once: a row's NSUB x 128 bytes together
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) load((bx * NSUB + sub) * kColW, all[sub]);
   // rows layout: the low half of each row's group word (blocks of the even subtile), stored whole, as one
   // 4-byte word, with the odd subtile's half (2-byte pieces were half-sector writes)
   uint32_t pend[2] = {0u, 0u};
   static_assert(NSUB % 2 == 0, "subtile pairs make whole scale groups");
-#pragma unroll 1
+#pragma unroll
   for (int sub = 0; sub < NSUB; ++sub) {
     const int64_t c0 = (bx * NSUB + sub) * kColW;
     uint4 cur[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
-    if (sub + 1 < NSUB) load(c0 + kColW, nxt);
+    for (int i = 0; i < NV; ++i) cur[i] = all[sub][i];
     __syncthreads();  // the previous subtile's reads of the tile and of obuf are done
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
