@@ -338,7 +338,8 @@ template <class C>
 __device__ __forceinline__ void epi_regs_swiglu_fwd_mx(const Acc<C>& acc, const FfnArgs& p, int64_t row0, int rows,
                                                        int n0, int lane, int wm, int wn, int wave, uint8_t* aq,
                                                        uint8_t* as, uint8_t* stage) {
-  static_assert(C::BN / 2 == 128 && C::BM * 4 <= 1024 * 4, "a tile's codes are 128-byte lines, its scales 1 KB");
+  static_assert(C::BN / 2 == 128, "a tile's 128 columns of A: whole 128-byte code lines, one scale group");
+  static_assert(C::BM * 128 + C::BM * 4 <= C::kLds * 2, "codes and scale words staged in the tile's LDS");
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   uint8_t* sq = stage;                  // [BM][128] codes, 16-byte chunks XOR-swizzled by row
   uint8_t* sw = stage + C::BM * 128;    // [BM] scale words

@@ -309,8 +309,8 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const T* __restrict__ src,
 // segment) and NSUB consecutive 64-column subtiles of them.  Each tile row names
 // its expert row and, through the routing's permutation, the token row it
 // copies (times the slot's gate for dY, rounded to bf16 as the combine backward
-// stores it); a subtile's loads are issued before the one before it is
-// encoded, so the scattered row reads stay in flight.  A subtile is quantised
+// stores it); every subtile's loads are issued before the first is encoded,
+// so a row's scattered pieces are in flight together.  A subtile is quantised
 // down the tokens exactly as mx_cols_kernel does with segments, and along d
 // into the rows layout as mx_cols_kernel's BOTH pass does (the workgroup writes
 // whole 128-byte lines of it); padding rows are zero in the token layout and

@@ -6,9 +6,10 @@
 // work minimal; the gains of MXFP8 came mostly from the expert FFN and from
 // moving data between experts, so these kernels are pure HBM streams.
 //
-// All four kernels are token-major: one wave owns one token, so each token row
-// is read (or written) exactly once and the k expert-buffer rows it touches are
-// whole 16-byte-vector rows.  Every access is a 16-byte vector, 1 KiB per wave
+// All four kernels are token-major: each token row is read (or written) exactly
+// once, by one wave (the combine and the dispatch backward: one wave per part of
+// 64 x 4 vectors of the row), and the k expert-buffer rows it touches are whole
+// 16-byte-vector rows.  Every access is a 16-byte vector, 1 KiB per wave
 // instruction.  The k row indices of a token are wave-uniform scalar loads.
 // Sums run in fp32 in slot order j = 0..k-1.
 #include "mx_common.hpp"

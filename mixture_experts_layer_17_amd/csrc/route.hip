@@ -6,13 +6,14 @@
 // Introduction: a fixed number of experts (four of 8 or 128) per token.
 //
 // Three launches, no host synchronisation and no atomics that decide an order:
-//  1. route_select: one wave per 64 tokens.  The 64 x E logit tile is staged
-//     through LDS with coalesced loads; each lane keeps a sorted top-k list of
-//     its token (logit descending, index ascending), writes indices and
-//     renormalised gates, then ORs its lane bit into a per-expert 64-bit mask.
-//     The rank of a token inside its block for expert e is the popcount of the
-//     mask bits below its lane (token order), and the block's count for e is
-//     the popcount of the whole mask.
+//  1. route_select: one workgroup per 64 tokens.  The 64 x E logit tile is
+//     staged through LDS with coalesced loads; one to four lanes per token each
+//     keep a sorted top-k list of a part of its row (logit descending, index
+//     ascending) and merge them over lane shuffles; the token's first lane writes
+//     indices and renormalised gates, then ORs the token's bit into a per-expert
+//     64-bit mask.  The rank of a token inside its block for expert e is the
+//     popcount of the mask bits below its own (token order), and the block's
+//     count for e is the popcount of the whole mask.
 //  2. route_scan: one workgroup turns the [blocks x E] count matrix into
 //     counts, offsets, MX block offsets and per-(block, expert) base rows.
 //  3. route_scatter: row = base[block][e] + rank; writes perm_dst and perm_src.
