@@ -13,7 +13,8 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets, int E, int BM,
-                                                       int64_t R, int64_t max_tiles, int4* __restrict__ tiles) {
+                                                       int64_t R, int64_t max_tiles, int4* __restrict__ tiles,
+                                                       int32_t* __restrict__ sched) {
   // tile counts per expert, their inclusive prefix sum (Hillis-Steele over
   // kMaxE = 256 entries), then one thread per table slot
   __shared__ int64_t cum[kMaxE];
@@ -65,28 +66,21 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
     if (n < 0) n = 0;
     tiles[max_tiles + 1 + tid] = make_int4(static_cast<int>(first), static_cast<int>(n), 0, 0);
   }
+  if (sched) {
+    // the backward's weight-gradient order (wgrad_tile_sorted): experts by cost ceil(n_e / 64) + 3 (K-steps plus
+    // an allowance for the epilogue), largest first, ties by lower index
+    __shared__ int32_t cost[kMaxE];
+    if (tid < E) cost[tid] = (n_s[tid] + 63) / 64 + 3;
+    __syncthreads();
+    if (tid < E) {
+      const int32_t c = cost[tid];
+      int rank = 0;
+      for (int e = 0; e < E; ++e) rank += (cost[e] > c || (cost[e] == c && e < tid)) ? 1 : 0;
+      sched[rank] = tid;
+    }
+  }
 }
 
-// One workgroup: each expert's cost, then its rank (the number of experts
-// ahead of it: costlier, or as costly with a lower index) is its slot.
-__global__ __launch_bounds__(256) void wgrad_sched_kernel(const int32_t* __restrict__ offsets, int E,
-                                                          int32_t* __restrict__ sched) {
-  __shared__ int32_t cost[kMaxE];
-  static_assert(kMaxE == 256, "one thread per expert");
-  const int t = threadIdx.x;
-  if (t < E) {
-    int32_t n = offsets[t + 1] - offsets[t];
-    if (n < 0) n = 0;
-    cost[t] = (n + 63) / 64 + 3;
-  }
-  __syncthreads();
-  if (t < E) {
-    const int32_t c = cost[t];
-    int rank = 0;
-    for (int e = 0; e < E; ++e) rank += (cost[e] > c || (cost[e] == c && e < t)) ? 1 : 0;
-    sched[rank] = t;
-  }
-}
 
 struct FfnShape {
   int64_t R;
@@ -148,13 +142,10 @@ unsigned persistent_grid(int occ, int64_t work) {
   return static_cast<unsigned>(g < w ? g : w);
 }
 
-void launch_wgrad_sched(const int32_t* offsets, int E, int32_t* sched, hipStream_t s) {
-  MOE_LAUNCH("wgrad_sched", wgrad_sched_kernel, dim3(1), dim3(256), 0, s, offsets, E, sched);
-}
 
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
-                     hipStream_t s) {
-  MOE_LAUNCH("tile_map", tile_map_kernel, dim3(1), dim3(256), 0, s, offsets, E, BM, R, max_tiles, tiles);
+                     hipStream_t s, int32_t* sched) {
+  MOE_LAUNCH("tile_map", tile_map_kernel, dim3(1), dim3(256), 0, s, offsets, E, BM, R, max_tiles, tiles, sched);
 }
 
 }  // namespace moe
@@ -217,7 +208,7 @@ extern "C" int moe_grouped_ffn_fwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   const int bm = tile_bm(prec, R, E);
   const int64_t mt = max_m_tiles(R, E, bm);
   int4* tiles = static_cast<int4*>(ws);
-  launch_tile_map(offsets, E, bm, R, mt, tiles, s);
+  launch_tile_map(offsets, E, bm, R, mt, tiles, s, nullptr);
   FfnArgs a{};
   a.offsets = offsets;
   a.tiles = tiles;
@@ -267,7 +258,9 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   const size_t tb = tiles_bytes(sh) + wgrad_sched_bytes();
   void* dhg = wsb + tb;
   void* dhu = wsb + tb + hbytes;
-  launch_tile_map(offsets, E, bm, R, mt, tiles, s);
+  // the tile table and, in the same launch, the weight gradients' expert order
+  int32_t* wsched = reinterpret_cast<int32_t*>(wsb + tiles_bytes(sh));
+  launch_tile_map(offsets, E, bm, R, mt, tiles, s, wsched);
   FfnArgs a{};
   a.offsets = offsets;
   a.tiles = tiles;
@@ -278,8 +271,6 @@ extern "C" int moe_grouped_ffn_bwd(int64_t R, int32_t E, int32_t d, int32_t f, i
   a.hg = h_gate; a.hu = h_up; a.act = a_act; a.dy = dy_perm;
   a.o_dhg = dhg; a.o_dhu = dhu; a.dhg = dhg; a.dhu = dhu;
   a.o_dx = dx_perm; a.o_dwg = dw_gate; a.o_dwu = dw_up; a.o_dwd = dw_down;
-  int32_t* wsched = reinterpret_cast<int32_t*>(wsb + tiles_bytes(sh));
-  launch_wgrad_sched(offsets, E, wsched, s);
   a.wsched = wsched;
   if (prec == MOE_MXFP8) {
     char* mxs = wsb + tb + 2 * hbytes;

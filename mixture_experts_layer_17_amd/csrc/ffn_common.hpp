@@ -87,7 +87,7 @@ __device__ __forceinline__ int64_t expert_tile(int64_t lid, int gx, const int4* 
 }
 
 // Weight-gradient tile order for one workgroup per tile (G4, G6), from the
-// experts sorted by cost (sched[0, E), as launch_wgrad_sched writes it).  The
+// experts sorted by cost (sched[0, E), as launch_tile_map writes it).  The
 // hardware deals workgroup ids round-robin over the 8 XCDs; id h runs on XCD
 // x = h % 8 as that XCD's q-th workgroup (q = h / 8).  The sorted experts go in
 // rounds of 8: in round 0 (the 8 costliest) each expert's tiles spread over all
@@ -118,11 +118,10 @@ inline int64_t wgrad_sorted_grid(int E, int ntile) {
 }
 
 // The experts sorted by weight-gradient cost, largest first (ties: lower
-// index), written by a one-workgroup kernel from the routing offsets so the
-// host never waits: sched[0, E) int32 on the device.  An expert's cost is
+// index), written on the device from the routing offsets (by the tile-table
+// launch) so the host never waits: sched[0, E) int32.  An expert's cost is
 // ceil(n_e / 64) + 3 (its K-steps plus an allowance for the epilogue).
 inline size_t wgrad_sched_bytes() { return align_up(static_cast<size_t>(kMaxE) * 4, 256); }
-void launch_wgrad_sched(const int32_t* offsets, int E, int32_t* sched, hipStream_t s);
 
 // Persistent launches (ffn.hip).  occupancy: resident workgroups per compute
 // unit of `kernel` at `threads` per workgroup (at least 1).  persistent_grid:
@@ -131,9 +130,10 @@ void launch_wgrad_sched(const int32_t* offsets, int E, int32_t* sched, hipStream
 int occupancy(const void* kernel, int threads);
 unsigned persistent_grid(int occ, int64_t work);
 
-// Launch the tile-table builder (defined in ffn.hip).
+// Launch the tile-table builder (defined in ffn.hip); with sched (not NULL) the
+// same launch also writes the weight gradients' expert order.
 void launch_tile_map(const int32_t* offsets, int E, int BM, int64_t R, int64_t max_tiles, int4* tiles,
-                     hipStream_t s);
+                     hipStream_t s, int32_t* sched);
 
 // GEMM launchers (defined in gemm_bf16.hip / gemm_f32.hip).
 int launch_ffn_bf16(int kind, const FfnArgs& a, int64_t max_tiles, hipStream_t s);
