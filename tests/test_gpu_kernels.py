@@ -30,7 +30,8 @@ def _adversarial(T, E, seed):
 
 ROUTE_CASES = [(1, 8, 2), (63, 8, 4), (64, 8, 4), (65, 16, 4), (1000, 128, 4), (4097, 256, 8), (200, 1, 1),
                (130, 8, 8), (16384, 128, 4),
-               (203, 1, 1), (7, 3, 2), (129, 5, 3)]  # logit tiles whose size is not a multiple of four
+               (203, 1, 1), (7, 3, 2), (129, 5, 3),  # logit tiles whose size is not a multiple of four
+               (97, 9, 2), (50, 7, 1), (33, 6, 3)]  # rows split unevenly over two or four scanning lanes
 
 
 @pytest.mark.parametrize("T,E,k", ROUTE_CASES)
